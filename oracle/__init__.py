@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for the attention forward pass (test infrastructure only).
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+may import this package; the product path never does.
+"""
+from .attention import (attention_probs_ref, attention_ref, attention_rows_ref,
+                        attention_tiled_ref, visible)
+
+__all__ = ["attention_probs_ref", "attention_ref", "attention_rows_ref",
+           "attention_tiled_ref", "visible"]

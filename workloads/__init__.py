@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module is shared by the oracle-side tests and the GPU-side tests and
+benchmark.  It only draws random numbers and rounds them to the storage dtype;
+it holds none of the attention arithmetic, so the oracle and the HIP path stay
+independent of each other.
+
+Recipe (applies to every workload):
+  * generator: ``numpy.random.Generator(PCG64(seed))``;
+  * draw order: Q, then K, then V, each ``standard_normal([B, H, S, d],
+    dtype=float32)`` in C order, multiplied by ``sigma``;
+  * rounding: round-to-nearest-even to the storage dtype (torch CPU ``.to``);
+  * optional outliers: after the three draws, for every (b, h) in (b, h)
+    order, ``rng.choice(S, floor(0.01 * S), replace=False)`` picks key rows that
+    are multiplied by 8 (a power of two, so scaling before or after rounding
+    gives identical bits).
+
+The named workloads are the five attention configurations the benchmark and
+the parity tests use (tiny fp32, causal d=64, long causal prefill d=128,
+sliding-window d=128, non-causal d=256 fp16) plus the outlier variant of the
+causal d=64 case.
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "generate", "input_digest",
+           "TORCH_DTYPES"]
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    S: int
+    d: int
+    dtype: str           # "f32" | "f16" | "bf16"
+    mask: str            # "none" | "causal" | "window"
+    window: int = 0      # keys visible to query i: i - window < j <= i
+    sigma: float = 1.0
+    seed: int = 0
+    outliers: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def visible_pairs(self) -> int:
+        """Number of (query, key) pairs the mask lets through, per (b, h) x B*H."""
+        S = self.S
+        if self.mask == "none":
+            per = S * S
+        elif self.mask == "causal":
+            per = S * (S + 1) // 2
+        else:
+            W = self.window
+            if W >= S:
+                per = S * (S + 1) // 2
+            else:
+                # rows i < W see i + 1 keys, the remaining S - W rows see W keys
+                per = W * (W + 1) // 2 + (S - W) * W
+        return per * self.B * self.H
+
+    def flops(self) -> float:
+        """Algorithmic forward FLOPs: 4*d per visible pair (2 for Q.K, 2 for P.V)."""
+        return 4.0 * self.d * self.visible_pairs()
+
+    def compulsory_bytes(self) -> int:
+        """Q, K, V read once plus O and the fp32 LSE written once."""
+        esz = {"f32": 4, "f16": 2, "bf16": 2}[self.dtype]
+        n = self.B * self.H * self.S
+        return 4 * n * self.d * esz + 4 * n
+
+
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 1, 2, 256, 64, "f32", "none", seed=1000),
+    "causal_d64": Workload("causal_d64", 2, 8, 1024, 64, "bf16", "causal", seed=1001),
+    "causal_d64_outliers": Workload("causal_d64_outliers", 2, 8, 1024, 64, "bf16",
+                                    "causal", seed=1001, outliers=True),
+    "prefill_8k_d128": Workload("prefill_8k_d128", 1, 32, 8192, 128, "bf16", "causal",
+                                seed=1002),
+    "window_18k_d128": Workload("window_18k_d128", 1, 16, 18432, 128, "bf16", "window",
+                                window=4096, seed=1003),
+    "full_d256_f16": Workload("full_d256_f16", 4, 16, 4096, 256, "f16", "none",
+                              sigma=0.5, seed=1004),
+}
+
+
+def make_inputs(B: int, H: int, S: int, d: int, dtype: str, seed: int,
+                sigma: float = 1.0, outliers: bool = False):
+    """Return (q, k, v) as contiguous CPU torch tensors of ``dtype``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, S, d)
+    arrs = []
+    for _ in range(3):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        arrs.append(x)
+    if outliers:
+        n_out = int(math.floor(0.01 * S))
+        kx = arrs[1]
+        for b in range(B):
+            for h in range(H):
+                idx = rng.choice(S, n_out, replace=False)
+                kx[b, h, idx, :] *= np.float32(8.0)
+    tdt = TORCH_DTYPES[dtype]
+    return tuple(torch.from_numpy(a).to(tdt).contiguous() for a in arrs)
+
+
+def generate(w: Workload):
+    return make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
+
+
+def input_digest(*tensors) -> str:
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.contiguous().view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()
+
+
+def with_shape(w: Workload, **kw) -> Workload:
+    return replace(w, **kw)
