@@ -1,0 +1,171 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+One step is one ``fa_fwd`` launch over the whole batch of the workload (all
+of the hot path: tile loads, QK^T, masking, online softmax, PV, epilogue).
+Inputs are generated once, copied to HBM and reused; W untimed steps, then K
+steps timed with events on the launch stream, bracketed by synchronisation.
+
+Prints one JSON line: the headline metric (forward TFLOP/s, causal FLOPs
+counted as 4*d per visible pair) plus a ``roofline`` object for the kernel and
+a ``cpu_baseline`` object (the fp64 oracle timed on a bounded sample of the
+same workload on the host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s at S=8K,d=128 bf16 causal; % of MFMA bf16 peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense: MFMA bf16/f16, fp32 vector
+HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "io_aware_tiled_flash_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; otherwise None."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, _, val = line.partition(":")
+            vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, target_s: float):
+    """Time the fp64 oracle on whole heads of the workload's own (host) inputs
+    until ~target_s of wall time has passed."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_ref
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    per_head_pairs = w.visible_pairs() // (w.B * w.H)
+    t0 = time.perf_counter()
+    heads = 0
+    while True:
+        b, h = divmod(heads, w.H)
+        attention_ref(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                      w.mask, w.window or None, w.scale)
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or heads >= w.B * w.H:
+            break
+    flops = 4.0 * w.d * per_head_pairs * heads
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (all {w.S} query rows each, "
+                      f"fp64 numpy, S and P materialised in 2048-row chunks), {el:.1f} s",
+            "seconds": round(el, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_8k_d128")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU-oracle sample (0 disables it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-head work needs no exchange; see the sharding notes in the design "
+              "document). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import io_aware_tiled_flash_amd as fa
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    host = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
+    q, k, v = (t.to(dev) for t in host)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    window = w.window or None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.forward(q, k, v, mask=w.mask, window=window, scale=w.scale, out=o, lse=lse,
+                   stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "d": w.d,
+                   "mask": w.mask, "window": w.window or None, "input_dtype": w.dtype,
+                   "kernel": fa.fa_query(w.d, fa.DTYPES[w.dtype], fa.MASKS[w.mask])},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": traffic},
+        "hbm": {"compulsory_bytes": w.compulsory_bytes(),
+                "compulsory_GBps": round(w.compulsory_bytes() / (ms * 1e-3) / 1e9, 1),
+                "peak_GBps": HBM_PEAK_GBS},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(w, *host, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

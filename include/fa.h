@@ -1,0 +1,120 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * The operation is exact attention O = softmax(scale * Q K^T) V evaluated tile
+ * by tile with the online softmax: a running row maximum m, a running
+ * denominator l, rescaling of an unnormalised output accumulator by
+ * exp(m_old - m_new) whenever the maximum grows, and a single division by l at
+ * the end, so that no score or probability matrix is ever written to device
+ * memory.  The method is the one described in "FlashAttention: Why Tiling
+ * Attention Makes Transformers Fast Without Changing the Result" (Dev.to),
+ * sections "Online softmax: correct as you go" and "The tiled forward pass",
+ * and in the aicomputerinstitute.com grade-12 chapter on flash attention,
+ * section "Tiling and the running (online) softmax".  Its interface (Q, K, V
+ * in device memory as [batch, heads, S, head_dim], a causal or sliding-window
+ * mask, output O plus a per-row logsumexp) follows the foundry.adhana.ai page
+ * "FlashAttention: IO-aware attention kernels", section "In and out".
+ *
+ * Every entry point is plain C: no C++ exception crosses it, no torch or HIP
+ * type appears in it, and it is safe to call from several host threads (error
+ * detail is kept per thread).
+ */
+#ifndef IO_AWARE_TILED_FLASH_FA_H
+#define IO_AWARE_TILED_FLASH_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+/* Element type of q, k, v and o.  lse is always fp32. */
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+/*
+ * Which keys j a query i may attend to (0-based positions, same sequence):
+ *   FA_MASK_NONE   every j in [0, S);
+ *   FA_MASK_CAUSAL j <= i;
+ *   FA_MASK_WINDOW i - window < j <= i  (window >= 1 counts the diagonal;
+ *                  window >= S is the causal mask).
+ * Causal and sliding-window masks are the kinds the foundry.adhana.ai page
+ * lists as natively supported ("The knobs", mask type); arbitrary boolean
+ * masks are deliberately not offered.
+ */
+typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW = 2 } fa_mask;
+
+typedef enum {
+  FA_OK = 0,
+  FA_EINVAL = 1,        /* an argument is invalid (see fa_fwd)                     */
+  FA_EUNSUPPORTED = 2,  /* valid request with no kernel; there is never a fallback */
+  FA_EHIP = 3           /* the HIP runtime reported an error on launch             */
+} fa_status;
+
+/*
+ * fa_fwd -- launch the attention forward pass on `stream`.
+ *
+ * q, k, v : device pointers, [B, H, S, d] contiguous (d fastest), element type
+ *           `dtype`.  Read only.
+ * o       : device pointer, [B, H, S, d] contiguous, `dtype`.  Written:
+ *           O[b,h,i,:] = sum_j P[i,j] V[b,h,j,:] with P the softmax over the
+ *           visible keys of scale * (Q[b,h,i,:] . K[b,h,j,:]), rounded to
+ *           nearest-even into `dtype`.
+ * lse     : device pointer, [B, H, S] fp32.  Written: natural-log logsumexp
+ *           of the visible scaled scores of each row (m + ln l).
+ * B, H, S, d : sizes, all >= 1.  Supported head sizes: d in {64, 128, 256}
+ *           for FA_F16 / FA_BF16; d in {64, 128} for FA_F32.
+ * mask, window : see fa_mask; `window` is read only for FA_MASK_WINDOW and
+ *           must then be >= 1.
+ * scale   : finite multiplier applied in fp32 to Q.K (callers usually pass
+ *           1/sqrt(d); there is no default inside the library).
+ * stream  : a hipStream_t (NULL = the null stream).
+ *
+ * Ownership: the caller owns every buffer; the library allocates, frees and
+ * copies nothing and keeps no pointer after returning.  The launch is
+ * asynchronous in stream order; completion is observed by synchronising the
+ * stream.  Results are deterministic: the same inputs give bit-identical
+ * outputs on every call (no atomics).
+ *
+ * Errors (all checked on the host before any HIP call, so they can be tested
+ * without a GPU; nothing is launched when one is returned):
+ *   FA_EINVAL      null pointer; a pointer not 16-byte aligned; B, H, S or d
+ *                  < 1; unknown dtype or mask; window < 1 with
+ *                  FA_MASK_WINDOW; non-finite scale; o overlapping q, k, v or
+ *                  lse, or lse overlapping q, k or v; a size whose byte count
+ *                  overflows, or a single head larger than 2 GiB.
+ *   FA_EUNSUPPORTED (dtype, d) without a kernel.
+ *   FA_EHIP        the launch failed; fa_last_error() holds the HIP message.
+ * With the environment variable FA_LOG=1 each call prints the chosen kernel
+ * and grid to stderr.
+ */
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int64_t B, int64_t H, int64_t S, int64_t d, int dtype, int mask,
+                 int64_t window, float scale, void *stream);
+
+/*
+ * fa_query -- name the kernel instance fa_fwd would launch for (d, dtype,
+ * mask), without launching anything or touching the GPU.  Writes a
+ * NUL-terminated name into kernel_name[0..len) (truncated if needed; may be
+ * NULL when len == 0).  Returns FA_OK, FA_EINVAL (bad enum or d < 1) or
+ * FA_EUNSUPPORTED (no kernel for that combination).
+ */
+fa_status fa_query(int64_t d, int dtype, int mask, char *kernel_name, size_t len);
+
+/* Static English text for a status code (never NULL). */
+const char *fa_status_str(int status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if
+ * none).  The string stays valid until the next fa_* call on that thread. */
+const char *fa_last_error(void);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IO_AWARE_TILED_FLASH_FA_H */

@@ -1,0 +1,155 @@
+"""MI355X (gfx950) exact-attention forward: Python binding of ``libfa.so``.
+
+The functions ``fa_fwd``, ``fa_query``, ``fa_status_str``, ``fa_last_error`` and
+``fa_abi_version`` mirror the C ABI declared in ``include/fa.h`` one to one
+(argument marshalling only).  ``forward`` is the tensor-level convenience
+wrapper: it checks the tensors, allocates ``o`` and ``lse`` with torch and
+launches on torch's current stream.  Every arithmetic step runs in the HIP
+kernels; there is no Python or CPU fallback, and a missing library is an
+error.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["FaError", "fa_fwd", "fa_query", "fa_status_str", "fa_last_error",
+           "fa_abi_version", "forward", "library_path", "DTYPES", "MASKS",
+           "FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
+
+FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+MASKS = {"none": 0, "causal": 1, "window": 2}
+ABI_VERSION = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfa.so"
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_status_text(status)}: {detail}" if detail else _status_text(status))
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FaError(FA_EHIP, f"{path} is missing; build it with "
+                               "`python -m io_aware_tiled_flash_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, c_int = ctypes.c_int64, ctypes.c_int
+    lib.fa_fwd.restype = c_int
+    lib.fa_fwd.argtypes = [ctypes.c_void_p] * 5 + [i64] * 4 + [c_int, c_int, i64,
+                                                               ctypes.c_float, ctypes.c_void_p]
+    lib.fa_query.restype = c_int
+    lib.fa_query.argtypes = [i64, c_int, c_int, ctypes.c_char_p, ctypes.c_size_t]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [c_int]
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_abi_version.restype = c_int
+    lib.fa_abi_version.argtypes = []
+    if lib.fa_abi_version() != ABI_VERSION:
+        raise FaError(FA_EHIP, f"ABI version {lib.fa_abi_version()} != {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return fa_status_str(status)
+    except FaError:
+        return f"status {status}"
+
+
+# ---- one-to-one mirrors of the C ABI --------------------------------------
+
+def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, d: int,
+           dtype: int, mask: int, window: int, scale: float, stream: int | None) -> int:
+    """Raw launch on device pointers; returns the fa_status code."""
+    return _load().fa_fwd(q, k, v, o, lse, B, H, S, d, dtype, mask, window,
+                          ctypes.c_float(scale), stream)
+
+
+def fa_query(d: int, dtype: int, mask: int) -> str:
+    buf = ctypes.create_string_buffer(128)
+    st = _load().fa_query(d, dtype, mask, buf, len(buf))
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return buf.value.decode()
+
+
+def fa_status_str(status: int) -> str:
+    return _load().fa_status_str(status).decode()
+
+
+def fa_last_error() -> str:
+    return _load().fa_last_error().decode()
+
+
+def fa_abi_version() -> int:
+    return _load().fa_abi_version()
+
+
+# ---- tensor-level wrapper --------------------------------------------------
+
+def _torch_dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: DTYPES["f32"], torch.float16: DTYPES["f16"],
+             torch.bfloat16: DTYPES["bf16"]}
+    if t.dtype not in codes:
+        raise FaError(FA_EINVAL, f"unsupported tensor dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def forward(q, k, v, mask: str = "none", window: int | None = None,
+            scale: float | None = None, out=None, lse=None, stream=None):
+    """Exact attention forward on [B, H, S, d] device tensors.
+
+    Returns (o, lse): o has q's shape and dtype, lse is fp32 [B, H, S] (natural
+    log).  ``scale`` defaults to 1/sqrt(d).  Launches on ``stream`` (a torch
+    stream) or torch's current stream; asynchronous like any torch op.
+    """
+    import torch
+    if mask not in MASKS:
+        raise FaError(FA_EINVAL, f"unknown mask {mask!r}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise FaError(FA_EINVAL, f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise FaError(FA_EINVAL, f"{name} must be a contiguous [B, H, S, d] tensor")
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise FaError(FA_EINVAL, "q, k, v must share shape and dtype")
+    if not (q.device == k.device == v.device):
+        raise FaError(FA_EINVAL, "q, k, v must be on one device")
+    B, H, S, d = q.shape
+    dt = _torch_dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise FaError(FA_EINVAL, "out must match q")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise FaError(FA_EINVAL, "lse must be a contiguous fp32 [B, H, S] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, S, d, dt, MASKS[mask], int(window or 0), float(scale),
+                    stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return out, lse

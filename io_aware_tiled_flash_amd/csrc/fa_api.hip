@@ -1,0 +1,170 @@
+// C ABI of the attention forward library: argument validation, choice of the
+// kernel instance, launch, and per-thread error text.
+//
+// Unsupported requests are errors, never a silent switch to a slower path:
+// the foundry.adhana.ai page "FlashAttention: IO-aware attention kernels"
+// (sections "Evals" and "Failure modes") describes such silent fallbacks as
+// the failure that corrupts measurements, and recommends logging which kernel
+// ran; FA_LOG=1 does that here.
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_err[512];
+
+fa_status fail(fa_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool log_enabled() {
+  static int cached = -1;
+  if (cached < 0) {
+    const char *e = getenv("FA_LOG");
+    cached = (e && e[0] && strcmp(e, "0") != 0) ? 1 : 0;
+  }
+  return cached == 1;
+}
+
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
+  const uint64_t x = (uint64_t)(uintptr_t)a, y = (uint64_t)(uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+
+// Resolve (dtype, d, mask) to a kernel; `launch` false only fills `info`.
+bool dispatch(int dtype, int d, int mask, const fa::FwdArgs *a, hipStream_t stream, bool launch,
+              fa::LaunchInfo *info, hipError_t *err) {
+  if (dtype == FA_F32) return fa::f32_forward(d, mask, a, stream, launch, info, err);
+  return fa::mfma_forward(dtype == FA_BF16 ? fa::kBF16 : fa::kF16, d, mask, a, stream, launch,
+                          info, err);
+}
+
+const char *dtype_name(int dt) {
+  return dt == FA_F32 ? "f32" : dt == FA_F16 ? "f16" : dt == FA_BF16 ? "bf16" : "?";
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                 int64_t H, int64_t S, int64_t d, int dtype, int mask, int64_t window,
+                 float scale, void *stream) {
+  g_err[0] = '\0';
+  if (!q || !k || !v || !o || !lse) return fail(FA_EINVAL, "null pointer argument");
+  const void *ptrs[5] = {q, k, v, o, lse};
+  for (int i = 0; i < 5; ++i)
+    if ((uintptr_t)ptrs[i] % 16 != 0)
+      return fail(FA_EINVAL, "pointer argument %d is not 16-byte aligned", i);
+  if (B < 1 || H < 1 || S < 1 || d < 1)
+    return fail(FA_EINVAL, "sizes must be >= 1 (B=%lld H=%lld S=%lld d=%lld)", (long long)B,
+                (long long)H, (long long)S, (long long)d);
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_EINVAL, "unknown dtype %d", dtype);
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_WINDOW)
+    return fail(FA_EINVAL, "unknown mask %d", mask);
+  if (mask == FA_MASK_WINDOW && window < 1)
+    return fail(FA_EINVAL, "window must be >= 1 for the sliding-window mask (got %lld)",
+                (long long)window);
+  if (!isfinite(scale)) return fail(FA_EINVAL, "scale must be finite");
+
+  const int64_t esz = dtype == FA_F32 ? 4 : 2;
+  int64_t bh, rows, elems, bytes, row_bytes, head_bytes, lse_bytes;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, S, &rows) || !mul_ok(rows, d, &elems) ||
+      !mul_ok(elems, esz, &bytes) || !mul_ok(rows, 4, &lse_bytes) ||
+      !mul_ok(d, esz, &row_bytes) || !mul_ok(S, row_bytes, &head_bytes))
+    return fail(FA_EINVAL, "tensor size overflows 64-bit byte counts");
+  if (head_bytes > (int64_t)INT32_MAX)
+    return fail(FA_EINVAL, "one head's [S, d] slab (%lld bytes) exceeds 2 GiB",
+                (long long)head_bytes);
+  if (bh > (int64_t)INT32_MAX || rows > (int64_t)INT64_MAX / 2)
+    return fail(FA_EINVAL, "batch*heads too large");
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) ||
+      overlaps(o, bytes, v, bytes) || overlaps(o, bytes, lse, lse_bytes))
+    return fail(FA_EINVAL, "output o overlaps an input or lse");
+  if (overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
+      overlaps(lse, lse_bytes, v, bytes))
+    return fail(FA_EINVAL, "lse overlaps an input");
+
+  // A window that covers the whole sequence is the causal mask.
+  int eff_mask = mask;
+  if (mask == FA_MASK_WINDOW && window >= S) eff_mask = FA_MASK_CAUSAL;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.S = (int)S;
+  a.window = eff_mask == FA_MASK_WINDOW ? (int)window : 0;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+
+  fa::LaunchInfo info = {nullptr, 0, 0};
+  hipError_t err = hipSuccess;
+  if (!dispatch(dtype, (int)d, eff_mask, &a, nullptr, false, &info, &err))
+    return fail(FA_EUNSUPPORTED, "no kernel for dtype=%s d=%lld (supported: bf16/f16 with d in "
+                "{64,128,256}; f32 with d in {64,128})", dtype_name(dtype), (long long)d);
+  const int64_t nq = (S + info.block_rows - 1) / info.block_rows;
+  if (nq * bh > (int64_t)INT32_MAX) return fail(FA_EINVAL, "grid too large");
+
+  if (log_enabled())
+    fprintf(stderr, "fa_fwd: kernel=%s grid=%lld block=%d B=%lld H=%lld S=%lld d=%lld\n",
+            info.name, (long long)(nq * bh), info.threads, (long long)B, (long long)H,
+            (long long)S, (long long)d);
+
+  dispatch(dtype, (int)d, eff_mask, &a, (hipStream_t)stream, true, &info, &err);
+  if (err != hipSuccess)
+    return fail(FA_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
+fa_status fa_query(int64_t d, int dtype, int mask, char *kernel_name, size_t len) {
+  g_err[0] = '\0';
+  if (d < 1) return fail(FA_EINVAL, "d must be >= 1");
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_EINVAL, "unknown dtype %d", dtype);
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_WINDOW)
+    return fail(FA_EINVAL, "unknown mask %d", mask);
+  if (len > 0 && !kernel_name) return fail(FA_EINVAL, "null name buffer");
+  fa::LaunchInfo info = {nullptr, 0, 0};
+  hipError_t err = hipSuccess;
+  if (d > INT32_MAX || !dispatch(dtype, (int)d, mask, nullptr, nullptr, false, &info, &err))
+    return fail(FA_EUNSUPPORTED, "no kernel for dtype=%s d=%lld", dtype_name(dtype),
+                (long long)d);
+  if (len > 0) {
+    strncpy(kernel_name, info.name, len - 1);
+    kernel_name[len - 1] = '\0';
+  }
+  return FA_OK;
+}
+
+const char *fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_EINVAL: return "FA_EINVAL: invalid argument";
+    case FA_EUNSUPPORTED: return "FA_EUNSUPPORTED: no kernel for this configuration";
+    case FA_EHIP: return "FA_EHIP: HIP runtime error";
+  }
+  return "unknown fa_status";
+}
+
+const char *fa_last_error(void) { return g_err; }
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP kernels against the fp64 oracle on identical seeded inputs.
+
+Bars (stated for this path): max |O_gpu - O_oracle| <= 2e-2 for bf16 inputs,
+5e-3 for fp16, 1e-5 for fp32; max |LSE_gpu - LSE_oracle| <= 1e-3.  Small shapes
+are compared element by element in full; the full-size workloads, launched
+exactly as the benchmark launches them, are compared on sampled rows the
+oracle computes one by one, plus properties that hold at any size.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_flash_amd as fa
+from oracle import attention_ref, attention_rows_ref
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-5}
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device (run with -m 'not gpu' on a host)")
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _run(q, k, v, mask, window, scale):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o, lse = fa.forward(qd, kd, vd, mask=mask, window=window, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def _check_full(q, k, v, mask, window, scale, dtype, label):
+    _say(label)
+    o, lse = _run(q, k, v, mask, window, scale)
+    o_ref, lse_ref = attention_ref(q, k, v, mask, window, scale)
+    do = np.abs(o.double().numpy() - o_ref).max()
+    dl = np.abs(lse.double().numpy() - lse_ref).max()
+    assert do <= O_TOL[dtype], f"{label}: max|dO| = {do}"
+    assert dl <= LSE_TOL, f"{label}: max|dLSE| = {dl}"
+    return o, lse
+
+
+def _sample_rows(S, n, rng):
+    edge = [0, 1, 2, 31, 32, 63, 64, 127, 128, S // 2, S - 2, S - 1]
+    rows = set(r for r in edge if 0 <= r < S)
+    rows.update(rng.choice(S, min(n, S), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def _check_sampled(q, k, v, o, lse, mask, window, scale, dtype, label, n_rows=48, seed=0):
+    rng = np.random.default_rng(seed)
+    B, H, S, d = q.shape
+    worst_o = worst_l = 0.0
+    for b in range(B):
+        for h in range(H):
+            rows = _sample_rows(S, n_rows, rng)
+            o_ref, lse_ref = attention_rows_ref(q[b, h], k[b, h], v[b, h], rows, mask, window,
+                                                scale)
+            worst_o = max(worst_o, np.abs(o[b, h, rows].double().numpy() - o_ref).max())
+            worst_l = max(worst_l, np.abs(lse[b, h, rows].double().numpy() - lse_ref).max())
+    assert worst_o <= O_TOL[dtype], f"{label}: sampled max|dO| = {worst_o}"
+    assert worst_l <= LSE_TOL, f"{label}: sampled max|dLSE| = {worst_l}"
+
+
+# --------------------------------------------------------------------------
+# the pages' worked example, through the kernel
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_worked_example_padded(dtype):
+    """q = [1, 0] over four keys in two tiles (aicomputerinstitute.com flash-
+    attention chapter, worked example), zero-padded to d = 64 and repeated
+    over 4 query rows; every value is a small integer, exact in all dtypes."""
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    q = torch.zeros(1, 1, 4, 64, dtype=tdt)
+    q[..., 0] = 1
+    k = torch.zeros(1, 1, 4, 64, dtype=tdt)
+    k[0, 0, :, :2] = torch.tensor([[1, 0], [0, 1], [3, 1], [-1, 1]], dtype=tdt)
+    v = torch.zeros(1, 1, 4, 64, dtype=tdt)
+    v[0, 0, :, :2] = torch.tensor([[1, 2], [3, 4], [5, 6], [7, 8]], dtype=tdt)
+    _say(f"worked example {dtype}")
+    o, lse = _run(q, k, v, "none", None, 1.0)
+    want = np.array([4.49786861, 5.49786861])
+    tol = O_TOL[dtype]
+    for i in range(4):
+        assert np.abs(o[0, 0, i, :2].double().numpy() - want).max() <= tol
+        assert float(o[0, 0, i, 2:].abs().max()) == 0.0
+        assert abs(float(lse[0, 0, i]) - (3.0 + math.log(1.2034379904932108))) <= LSE_TOL
+
+
+# --------------------------------------------------------------------------
+# the named workloads
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_f32", "causal_d64", "causal_d64_outliers"])
+def test_small_workloads_full(name):
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
+    _check_full(q, k, v, w.mask, w.window or None, w.scale, w.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["prefill_8k_d128", "window_18k_d128", "full_d256_f16"])
+def test_large_workloads_sampled(name):
+    w = WORKLOADS[name]
+    _say(f"{name}: generating inputs")
+    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
+    _say(f"{name}: launching")
+    o, lse = _run(q, k, v, w.mask, w.window or None, w.scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    # |O| is a convex combination of V rows, so it never exceeds max |V|
+    assert float(o.float().abs().max()) <= float(v.float().abs().max()) * (1 + 1e-2)
+    if w.mask != "none":  # causal/window row 0 sees only key 0
+        s00 = (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1) * w.scale
+        assert float((lse[:, :, 0].double() - s00).abs().max()) <= LSE_TOL
+        assert float((o[:, :, 0].float() - v[:, :, 0].float()).abs().max()) == 0.0
+    _say(f"{name}: oracle rows")
+    _check_sampled(q, k, v, o, lse, w.mask, w.window or None, w.scale, w.dtype, name)
+
+
+# --------------------------------------------------------------------------
+# shapes, masks, ragged tails
+# --------------------------------------------------------------------------
+
+GRID = [(dt, d, m) for dt in ("bf16", "f16") for d in (64, 128, 256)
+        for m in ("none", "causal", "window")]
+
+
+@pytest.mark.parametrize("dtype,d,mask", GRID)
+@pytest.mark.parametrize("S", [1, 100, 257])
+def test_grid_full(dtype, d, mask, S):
+    window = 37 if mask == "window" else None
+    q, k, v = make_inputs(1, 3, S, d, dtype, seed=S * 7 + d)
+    _check_full(q, k, v, mask, window, 1.0 / math.sqrt(d), dtype,
+                f"grid {dtype} d={d} {mask} S={S}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "window"])
+@pytest.mark.parametrize("S", [1, 77, 300])
+def test_f32_full(d, mask, S):
+    window = 20 if mask == "window" else None
+    q, k, v = make_inputs(2, 1, S, d, "f32", seed=S + d)
+    _check_full(q, k, v, mask, window, 1.0 / math.sqrt(d), "f32", f"f32 d={d} {mask} S={S}")
+
+
+@pytest.mark.parametrize("S,mask,window", [(1000, "causal", None), (4097, "none", None),
+                                           (4097, "window", 700), (2049, "causal", None)])
+def test_ragged_lengths(S, mask, window):
+    q, k, v = make_inputs(1, 2, S, 128, "bf16", seed=S)
+    _check_full(q, k, v, mask, window, 1.0 / math.sqrt(128), "bf16", f"ragged S={S} {mask}")
+
+
+def test_many_heads_small_sequence():
+    q, k, v = make_inputs(3, 40, 65, 64, "bf16", seed=5)
+    _check_full(q, k, v, "causal", None, 0.125, "bf16", "B=3 H=40 S=65")
+
+
+@pytest.mark.parametrize("scale", [0.01, 1.0, 4.0])
+def test_scale_values(scale):
+    q, k, v = make_inputs(1, 2, 300, 128, "f16", seed=11)
+    _check_full(q, k, v, "causal", None, scale, "f16", f"scale={scale}")
+
+
+# --------------------------------------------------------------------------
+# special cases with closed forms
+# --------------------------------------------------------------------------
+
+def test_zero_keys_average_visible_values():
+    S = 200
+    q, k, v = make_inputs(1, 2, S, 128, "bf16", seed=12)
+    k = torch.zeros_like(k)
+    _say("zero keys")
+    o, lse = _run(q, k, v, "causal", None, 0.088)
+    cum = torch.cumsum(v.double(), dim=2) / torch.arange(1, S + 1, dtype=torch.float64)[:, None]
+    assert float((o.double() - cum).abs().max()) <= O_TOL["bf16"]
+    want = torch.log(torch.arange(1, S + 1, dtype=torch.float64))
+    assert float((lse.double() - want).abs().max()) <= LSE_TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_window_of_one_returns_values(dtype):
+    d = 64
+    q, k, v = make_inputs(1, 2, 150, d, dtype, seed=13)
+    _say(f"window=1 {dtype}")
+    o, lse = _run(q, k, v, "window", 1, 0.125)
+    assert torch.equal(o, v)
+    s = (q.double() * k.double()).sum(-1) * 0.125
+    assert float((lse.double() - s).abs().max()) <= LSE_TOL
+
+
+def test_window_covering_sequence_is_causal_bitwise():
+    q, k, v = make_inputs(1, 2, 333, 128, "bf16", seed=14)
+    _say("window >= S")
+    oc, lc = _run(q, k, v, "causal", None, 0.088)
+    for W in (333, 334, 10_000):
+        ow, lw = _run(q, k, v, "window", W, 0.088)
+        assert torch.equal(ow, oc) and torch.equal(lw, lc)
+
+
+def test_window_one_less_than_sequence():
+    q, k, v = make_inputs(1, 2, 333, 128, "bf16", seed=15)
+    _check_full(q, k, v, "window", 332, 0.088, "bf16", "window S-1")
+
+
+def test_deterministic_repeat():
+    w = WORKLOADS["causal_d64_outliers"]
+    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
+    _say("determinism")
+    runs = [_run(q, k, v, "causal", None, w.scale) for _ in range(3)]
+    for o, lse in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(lse, runs[0][1])
+
+
+def test_outputs_do_not_touch_neighbours():
+    """The kernel writes exactly o and lse: guard bands around them stay intact."""
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_inputs(1, 2, 130, 64, "bf16", seed=16))
+    big = torch.full((3 * q.numel(),), 7.0, dtype=torch.bfloat16, device=dev)
+    out = big[q.numel():2 * q.numel()].view_as(q)
+    lbig = torch.full((3 * 260,), 9.0, dtype=torch.float32, device=dev)
+    lse = lbig[260:520].view(1, 2, 130)
+    _say("guard bands")
+    fa.forward(q, k, v, mask="causal", out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((big[:q.numel()] == 7.0).all()) and bool((big[2 * q.numel():] == 7.0).all())
+    assert bool((lbig[:260] == 9.0).all()) and bool((lbig[520:] == 9.0).all())
