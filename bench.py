@@ -84,6 +84,26 @@ def cpu_baseline(w, q, k, v, target_s: float):
             "seconds": round(el, 2)}
 
 
+def copy_calibration(args) -> int:
+    """Plain copy of a known byte count per step, for scaling HBM counters."""
+    import torch
+    n = args.copy_calibration_mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(json.dumps({"copy_bytes_read_per_step": n, "copy_bytes_written_per_step": n,
+                      "ms_per_step": round(ms, 4), "GBps": round(2 * n / ms / 1e6, 1)}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +112,9 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill_8k_d128")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of attention, run a plain device-to-device copy of this "
+                         "many MiB per step (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -109,6 +132,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
+    if args.copy_calibration_mib > 0:
+        return copy_calibration(args)
     dev = torch.device("cuda:0")
     host = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
     q, k, v = (t.to(dev) for t in host)
