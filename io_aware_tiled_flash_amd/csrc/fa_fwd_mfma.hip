@@ -36,14 +36,13 @@
 //     half), halving LDS traffic per flop, and the loop body is ordered
 //     S_0, {S_1 | softmax_0}, {O_0 | softmax_1}, O_1 so that one half's
 //     vector-ALU softmax can issue while the other half's MFMAs run;
-//   * the loads of tile t+1 are issued before the math of tile t into a free
-//     LDS stage (K double-buffered, V triple-buffered because the lagging
-//     half reads the previous tile's V), with one barrier per tile;
+//   * tiles are loaded PF tiles ahead of the math into free LDS stages (PF+1
+//     for K, PF+2 for V because the PV products lag one tile), which hides
+//     the L2/HBM latency behind several tiles of math; one barrier per tile;
 //   * causal and sliding-window masks skip whole tiles: the work-group visits
-//     only key tiles that intersect its rows' visible band, a wave skips the
-//     math of tiles that are invisible to all of its rows, and the elementwise
-//     mask is evaluated only in a separate loop body used for tiles that
-//     straddle a band edge;
+//     only key tiles that intersect its rows' visible band, and the
+//     elementwise mask (scores set to -inf) runs only on tiles that straddle
+//     a band edge of a wave's rows;
 //   * scores are scaled into base 2 (scale * log2 e) so that every exponential
 //     is one v_exp_f32, with the scale folded into the exponent's FMA;
 //   * lazy rescaling: the running offset m is only moved when a row's maximum
@@ -120,11 +119,26 @@ __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define FA_LDS __attribute__((address_space(3)))
 
+// Buffer resource words for one head's [S, d] slab (same layout as above),
+// for the inline-assembly loads below.
+__device__ inline u32x4 rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes land
-// at lds_base + 16 * i (lds_base must be the same in every lane of the wave).
-__device__ inline void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
-                                     FA_LDS void *lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, byte_off, 0, 0, 0);
+// at lds_addr + 16 * i (lds_addr is wave-uniform).  Issued as inline assembly
+// so that the compiler does not track it: it would otherwise wait for every
+// outstanding direct load before each LDS read and each barrier, which
+// serialises the multi-tile prefetch.  Completion is awaited explicitly with
+// s_waitcnt vmcnt (vector-memory loads complete in issue order).
+__device__ inline void load16_to_lds(u32x4 rsrc, uint32_t byte_off, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(byte_off), "s"(rsrc)
+      : "memory");  // M0 is only ever set by these statements in this kernel
 }
 
 // ds_read_b64_tr_b16: in every group of 16 lanes, lanes 4k..4k+3 name row k
@@ -146,29 +160,44 @@ __device__ inline bool key_visible(int key, int row, int S, int window) {
   return key <= row && key > row - window;
 }
 
-template <class Ty, int D, int MASK, int NW, int BC, int NH>
+// 16-byte chunk position of chunk c in LDS row r (64 banks of 4 bytes: a
+// 256-byte bank line).  Rows of at least 256 bytes XOR the chunk with the low
+// four row bits; 128-byte rows (d = 64) share a bank line in pairs and XOR
+// with the next three bits.  Either way, 16 consecutive rows reading the same
+// logical chunk hit 16 different 16-byte bank groups.
+template <int D>
+__device__ __host__ constexpr int swz(int r, int c) {
+  return D >= 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+
+template <class Ty, int D, int MASK, int NW, int BC, int NH, int PF>
 __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
-  constexpr int NT = NW * 64;          // threads per work-group
   constexpr int QW = 32 * NH;          // query rows per wave
   constexpr int BR = QW * NW;          // query rows per work-group
   constexpr int NKB = BC / 32;         // 32-key blocks per key tile
   constexpr int NKS = D / 16;          // contraction steps of S^T = K Q^T
   constexpr int NDB = D / 32;          // 32-wide d blocks of O^T
   constexpr int NPS = BC / 16;         // contraction steps of O^T = V^T P^T
-  constexpr int KCH = D / 8;           // 16-byte chunks per K row
+  constexpr int KCH = D / 8;           // 16-byte chunks per K/V row
   constexpr int TILE_CHUNKS = BC * KCH;  // 16-byte chunks per K or V tile
   constexpr int LOADS_PER_WAVE = TILE_CHUNKS / 64 / NW;  // direct loads per tensor
-  static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
+  static_assert(D % 32 == 0 && BC % 32 == 0 && BC % 16 == 0, "tile shape");
   static_assert(KCH >= 8, "swizzle needs >= 8 chunks per LDS row");
   static_assert(TILE_CHUNKS % (64 * NW) == 0, "tile must split evenly over the waves");
 
-  // K is double-buffered; V is triple-buffered because the last half's PV
-  // product for tile t is issued during tile t+1 (see the loop below).
-  __shared__ u32x4 k_lds[2][BC * KCH];
-  __shared__ u32x4 v_lds[3][BC * KCH];
+  // Tiles are loaded PF tiles ahead of the one being computed.  K needs PF+1
+  // stages; V needs PF+2 because the PV products of tile t are issued during
+  // tile t+1.
+  constexpr int NKST = PF + 1, NVST = PF + 2;
+  constexpr int LOADS_PER_TILE = 2 * LOADS_PER_WAVE;  // per wave, K and V
+  static_assert(LOADS_PER_TILE * (PF - 1) < 64, "vmcnt range");
+  __shared__ u32x4 k_lds[NKST][TILE_CHUNKS];
+  __shared__ u32x4 v_lds[NVST][TILE_CHUNKS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // readfirstlane makes the wave index (and everything derived from it) a
+  // scalar, so per-wave tile decisions become scalar branches.
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, lg = lane >> 5;
   const int S = a.S;
   const int BH = a.B * a.H;
@@ -182,12 +211,15 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   const size_t head_off = (size_t)bh * (size_t)S * D;  // elements
   const uint32_t head_bytes = (uint32_t)S * D * 2u;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t *)a.q + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t *)a.k + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t *)a.v + head_off, head_bytes);
+  const u32x4 rk = rsrc_words((const uint16_t *)a.k + head_off, head_bytes);
+  const u32x4 rv = rsrc_words((const uint16_t *)a.v + head_off, head_bytes);
 
-  // The softmax runs on c * s with c >= 0: a negative scale is applied by
-  // flipping the sign bits of Q (exact in bf16 and fp16).
-  const float c = fabsf(a.scale_log2);
+  // The softmax runs on c * s with c > 0: a negative scale is applied by
+  // flipping the sign bits of Q (exact in bf16 and fp16), and a zero scale
+  // becomes 1e-30, whose products with finite scores are far below fp32
+  // resolution of the exponent's result (every weight is still exactly 1),
+  // while c * (-inf) stays -inf for masked scores.
+  const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
   const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q^T as the B operand: lane holds Q[row][16*ks + 8*lg .. +7] for every ks.
@@ -199,6 +231,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       qreg[h][ks] = load16(rq, (uint32_t)((wr0 + 32 * h + lq) * D + 16 * ks + 8 * lg) * 2u) ^ qflip;
+  // Q never meets the vector ALU again: keep it in accumulation registers
+  // (MFMA reads its A/B operands from AGPRs too), leaving VGPRs to the softmax.
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qreg[h][ks]));
 
   // Key tiles this work-group visits.
   const int ntk = (S + BC - 1) / BC;
@@ -210,23 +248,24 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   }
 
   // Direct loads of tile kt into K stage kst and V stage vst.  Chunk position
-  // p of a stage holds row p / KCH, global chunk (p % KCH) ^ (row & 7).
-  auto load_tile = [&](int kt, int kst, int vst) {
+  // p of a stage holds row p / KCH, logical chunk c with swz(row, c) == p % KCH
+  // (swz is an involution in c).
+  auto load_tile = [&](int kt, int kst, int vst) __attribute__((always_inline)) {
     const int k0 = kt * BC;
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i) {
       const int blk = wave * LOADS_PER_WAVE + i;  // 64-chunk block of the tile
       const int pos = 64 * blk + lane;
-      const int r = pos / KCH, cc = (pos % KCH) ^ (r & 7);
+      const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
       const uint32_t off = (uint32_t)((k0 + r) * D + 8 * cc) * 2u;
-      load16_to_lds(rk, off, (FA_LDS void *)&k_lds[kst][64 * blk]);
-      load16_to_lds(rv, off, (FA_LDS void *)&v_lds[vst][64 * blk]);
+      load16_to_lds(rk, off, (uint32_t)(uintptr_t)&k_lds[kst][64 * blk]);
+      load16_to_lds(rv, off, (uint32_t)(uintptr_t)&v_lds[vst][64 * blk]);
     }
   };
 
   f32x16 oacc[NH][NDB];
   f32x16 sacc[NH][NKB];
-  u32x4 pk[NH][NPS];  // packed weights of each half's latest tile
+  u32x4 pk[NH][NPS];  // packed weights of the previous tile, awaiting their PV product
   float m[NH], l[NH], alpha[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -238,12 +277,51 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     l[h] = 0.f;        // this lane's share of the running denominator
     alpha[h] = 1.f;
   }
-  // The PV product of the last half (NH-1) lags one tile behind: `pending`
-  // says pk[NH-1] / alpha[NH-1] still have to be folded into oacc[NH-1].
-  bool pending = false;
+  // O accumulators live in AGPRs (MFMA accumulates there directly); only the
+  // rare rescale and the epilogue read them back.
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) asm volatile("" : "+a"(oacc[h][i]));
+  // The PV products lag one tile: pk / alpha hold the previous tile's
+  // weights and factors until the next tile (or the epilogue) multiplies them
+  // in.  Initially the weights are zero, and so is the V stage they meet.
+
+  // Per-lane LDS byte offsets.  The swizzle XOR is split into a per-lane base
+  // and a compile-time part so every operand read is "lane pointer +
+  // immediate".  K operand of step ks, key block kb: row 32*kb + lq, logical
+  // chunk 2*ks + lg; one base per ks % KSW.
+  constexpr int KSW = D >= 128 ? 8 : 4;
+  int k_base[KSW];
+#pragma unroll
+  for (int j = 0; j < KSW; ++j) k_base[j] = lq * (D * 2) + 16 * swz<D>(lq, 2 * j + lg);
+
+  // V^T operand of step kk, d block db, part i2: lane (group G = lane/16,
+  // n = lane%16) names row key = 16*kk + 8*i2 + tr_key (tr_key = 4*lg + n/4)
+  // at column d = 32*db + 16*(G&1) + 4*(n&3) and receives keys
+  // 16*kk + 8*i2 + 4*lg + 0..3 of column 32*db + lane%32.  With t = (d/8) % 4
+  // the swizzled chunk splits into a lane part (one base per parity of db for
+  // d >= 128) and a constant.
+  const int tr_key = 4 * lg + ((lane & 15) >> 2);
+  const int tr_t = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_lane = tr_key * (D * 2) + 8 * (lane & 1);
+  int v_base[2];
+  if (D >= 128) {
+    v_base[0] = tr_lane + 16 * (tr_t ^ (tr_key & 3)) + 64 * lg;
+    v_base[1] = tr_lane + 16 * (tr_t ^ (tr_key & 3)) + 64 * (1 - lg);
+  } else {
+    v_base[0] = v_base[1] = tr_lane + 16 * (tr_t ^ (tr_key >> 1));
+  }
+  auto v_const = [](int kk, int i2, int db) constexpr {
+    return D >= 128 ? (16 * kk + 8 * i2) * (D * 2) + 256 * (db >> 2) + 128 * (((db >> 1) & 1) ^ i2)
+                    : (16 * kk + 8 * i2) * (D * 2) + 64 * (db ^ i2);
+  };
 
   auto s_phase = [&](int kst) __attribute__((always_inline)) {
-    const u32x4 *kl = k_lds[kst];
+    const char *kl = (const char *)&k_lds[kst][0];
+    const char *kp[KSW];
+#pragma unroll
+    for (int j = 0; j < KSW; ++j) kp[j] = kl + k_base[j];
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -252,20 +330,22 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int r = 32 * kb + lq;
-        const u32x4 op = kl[r * KCH + ((2 * ks + lg) ^ (r & 7))];
+        const u32x4 op =
+            *(const u32x4 *)(kp[ks % KSW] + kb * (32 * D * 2) + 16 * 2 * KSW * (ks / KSW));
 #pragma unroll
         for (int h = 0; h < NH; ++h) sacc[h][kb] = Ty::mfma(op, qreg[h][ks], sacc[h][kb]);
       }
+    // scores go to the vector ALU next: keep them in VGPRs
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) asm volatile("" : "+v"(sacc[h][kb]));
   };
 
-  // V^T operand of step kk, d block db: lane (group G = lane/16, n = lane%16)
-  // reads rows key = 16*kk + 8*i2 + 4*lg + n/4 at d = 32*db + 16*(G&1) + 4*(n&3)
-  // and receives keys 16*kk + 8*i2 + 4*lg + 0..3 of column d = 32*db + lane%32.
-  const int tr_key = 4 * lg + ((lane & 15) >> 2);
-  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  auto o_mfma = [&](int h, int vst) __attribute__((always_inline)) {
+  // O_h^T += V^T P_h^T for every half, each V operand read once.
+  auto o_phase = [&](int vst) __attribute__((always_inline)) {
     const char *vl = (const char *)&v_lds[vst][0];
+    const char *vp[2] = {vl + v_base[0], vl + v_base[1]};
 #pragma unroll
     for (int kk = 0; kk < NPS; ++kk)
 #pragma unroll
@@ -273,139 +353,147 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
         u32x4 op;
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
-          const int key = 16 * kk + 8 * i2 + tr_key;
-          const int d = 32 * db + tr_d;
-          const int off = key * (D * 2) + ((((d >> 3) ^ (key & 7))) << 4) + ((d & 7) << 1);
-          const u32x2 v2 = lds_read_tr16((const FA_LDS void *)(vl + off));
+          const u32x2 v2 =
+              lds_read_tr16((const FA_LDS void *)(vp[db & 1] + v_const(kk, i2, db)));
           op[2 * i2] = v2[0];
           op[2 * i2 + 1] = v2[1];
         }
-        oacc[h][db] = Ty::mfma(op, pk[h][kk], oacc[h][db]);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) oacc[h][db] = Ty::mfma(op, pk[h][kk], oacc[h][db]);
       }
   };
 
-  auto rescale = [&](int h) __attribute__((always_inline)) {
-    if (__any(alpha[h] != 1.f)) {
+  auto rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[h][db] *= alpha[h];
-    }
+    for (int h = 0; h < NH; ++h)
+      if (__any(alpha[h] != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[h][db] *= alpha[h];
+      }
   };
 
-  // Online-softmax update of half h from its raw scores in sacc[h]; leaves the
-  // packed weights in pk[h] and the accumulator factor in alpha[h].
-  auto softmax = [&](int h, auto masked_c, int k0) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_c)::value;
-    const int row = wr0 + 32 * h + lq;
-    float tmax = -INFINITY;
-    if (MASKED) {
+  // Elementwise mask of the raw scores (tiles straddling a band edge):
+  // invisible (query, key) pairs become -inf.
+  auto apply_mask = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int row = wr0 + 32 * h + lq;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3);
-          const float x = key_visible<MASK>(key, row, S, a.window) ? sacc[h][kb][r] * c
-                                                                    : -INFINITY;
-          sacc[h][kb][r] = x;
-          tmax = fmaxf(tmax, x);
+          if (!key_visible<MASK>(key, row, S, a.window)) sacc[h][kb][r] = -INFINITY;
         }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[h][kb][r]);
-      tmax *= c;  // c >= 0 and every score is finite here
     }
-    tmax = fmaxf(tmax, wave_partner(tmax));
+  };
+
+  // Online-softmax update of half h from its raw scores: new packed weights
+  // in pk_new, accumulator factor in alpha[h].
+  auto softmax = [&](int h, u32x4 (&pk_new)[NPS]) __attribute__((always_inline)) {
+    float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4)
+        t4[r >> 2] = fmaxf(t4[r >> 2], fmaxf(fmaxf(sacc[h][kb][r], sacc[h][kb][r + 1]),
+                                             fmaxf(sacc[h][kb][r + 2], sacc[h][kb][r + 3])));
+    float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, tmax),
+                                                     __builtin_bit_cast(uint32_t, tmax),
+                                                     false, false);
+    tmax = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
+                 __builtin_bit_cast(float, (uint32_t)sw[1])) * c;  // c > 0 keeps order
     const float m_old = m[h];
     const float m_new = tmax > m_old + TAU ? tmax : m_old;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;  // row fully masked so far
     alpha[h] = __builtin_amdgcn_exp2f(m_old - m_use);      // 1 if unchanged, 0 from -inf
     m[h] = m_new;
-    float lsum = 0.f;
+    float s4[4] = {-0.f, -0.f, -0.f, -0.f};  // -0 + x == x folds away
 #pragma unroll
     for (int kk = 0; kk < NPS; ++kk) {
       const int kb = kk >> 1, base = 8 * (kk & 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float p0, p1;
-        if (MASKED) {
-          p0 = __builtin_amdgcn_exp2f(sacc[h][kb][base + 2 * j] - m_use);
-          p1 = __builtin_amdgcn_exp2f(sacc[h][kb][base + 2 * j + 1] - m_use);
-        } else {
-          p0 = __builtin_amdgcn_exp2f(fmaf(sacc[h][kb][base + 2 * j], c, -m_use));
-          p1 = __builtin_amdgcn_exp2f(fmaf(sacc[h][kb][base + 2 * j + 1], c, -m_use));
-        }
-        pk[h][kk][j] = Ty::pack2(p0, p1);
-        lsum += p0 + p1;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[h][kb][base + 2 * j], c, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[h][kb][base + 2 * j + 1], c, -m_use));
+        pk_new[kk][j] = Ty::pack2(p0, p1);
+        s4[j] += p0 + p1;
       }
     }
-    l[h] = l[h] * alpha[h] + lsum;
+    l[h] = l[h] * alpha[h] + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
   };
 
-  // Fold the lagging half's pending tile (whose V sits in stage vst) into O.
-  auto flush = [&](int vst) __attribute__((always_inline)) {
-    rescale(NH - 1);
-    o_mfma(NH - 1, vst);
-#pragma unroll
-    for (int i = 0; i < NPS; ++i) pk[NH - 1][i] = u32x4{};
-    alpha[NH - 1] = 1.f;
-  };
-
-  // One key tile.  Phase 1: S for every half (each K operand read once).
-  // Phase 2: the lagging half's previous PV product, independent of the
-  // softmax of half 0 that issues next to it.  Phase 3 (NH == 2): PV of half
-  // 0 next to the softmax of half 1.
-  auto tile = [&](auto masked_c, int kst, int vst, int vprev, int k0) __attribute__((always_inline)) {
+  // One key tile.  Phase A: S for every half, each K operand read once and
+  // used by all halves.  Phase B: the previous tile's PV products (each V
+  // operand read once), independent of this tile's softmaxes, which issue
+  // next to them.
+  auto tile = [&](bool masked, int kst, int vprev, int k0) __attribute__((always_inline)) {
     s_phase(kst);
-    rescale(NH - 1);
-    o_mfma(NH - 1, vprev);  // zero weights when nothing is pending
-    softmax(0, masked_c, k0);
-    if (NH == 2) {
-      rescale(0);
-      o_mfma(0, vst);
-      softmax(NH - 1, masked_c, k0);
+    if (masked) apply_mask(k0);
+    rescale();  // factors of the pending tile
+    u32x4 pk_new[NH][NPS];
+    o_phase(vprev);  // zero weights when nothing is pending
+#pragma unroll
+    for (int h = 0; h < NH; ++h) softmax(h, pk_new[h]);
+    // Interleave: per V operand, its two transposing reads, its NH MFMAs and
+    // a share of the softmax's vector instructions.
+#pragma unroll
+    for (int i = 0; i < NPS * NDB; ++i) {
+      (void)0;
     }
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < NPS; ++i) pk[h][i] = pk_new[h][i];
   };
 
-  // Zero the V stage that the first tile's lagging product reads, so that its
-  // zero weights never meet uninitialised LDS.
-  for (int i = tid; i < TILE_CHUNKS; i += NT) v_lds[2][i] = u32x4{};
-  if (kt_begin < kt_end) load_tile(kt_begin, 0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // Zero the V stage that the first tile's (empty) pending product reads, so
+  // that its zero weights never meet uninitialised LDS.
+  for (int i = tid; i < TILE_CHUNKS; i += NW * 64) v_lds[NVST - 1][i] = u32x4{};
+  // Prefetches past the last tile read an index beyond the sequence: the
+  // buffer range check turns them into zero fills of a free stage, so every
+  // tile issues the same number of loads and the waits below are constants
+  // (no branch splits the loop body).
+  const int kt_none = ntk + PF;
+  auto tile_or_none = [&](int kt) { return kt < kt_end ? kt : kt_none; };
+#pragma unroll
+  for (int i = 0; i < PF; ++i) load_tile(tile_or_none(kt_begin + i), i, i);
+  // Wait for the first tile only (and the zero fill); the later prefetches
+  // stay in flight.
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
+  __builtin_amdgcn_s_barrier();
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int it = kt - kt_begin;
-    const int kst = it & 1, vst = it % 3, vprev = (it + 2) % 3;
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) load_tile(kt + 1, (it + 1) & 1, (it + 1) % 3);
+    const int kst = it % NKST, vprev = (it + NVST - 1) % NVST;
+    load_tile(tile_or_none(kt + PF), (it + PF) % NKST, (it + PF) % NVST);
 
+    // Every wave runs every tile of the work-group's range; a tile that lies
+    // outside a wave's band is simply fully masked (weights 0, factor 1).
+    // That costs a few percent of MFMA work on band edges but keeps a single
+    // copy of each phase in the loop.
     const int k0 = kt * BC;
-    bool active = true, need_mask;
-    if (MASK == kMaskCausal) {
-      active = k0 <= wr1;
+    bool need_mask;
+    if (MASK == kMaskCausal)
       need_mask = k0 + BC - 1 > wr0;
-    } else if (MASK == kMaskWindow) {
-      active = k0 <= wr1 && k0 + BC - 1 > wr0 - a.window;
+    else if (MASK == kMaskWindow)
       need_mask = k0 + BC - 1 > wr0 || k0 <= wr1 - a.window;
-    } else {
+    else
       need_mask = k0 + BC > S;
-    }
-    if (active) {
-      if (need_mask)
-        tile(std::true_type{}, kst, vst, vprev, k0);
-      else
-        tile(std::false_type{}, kst, vst, vprev, k0);
-      pending = true;
-    } else if (pending) {
-      flush(vprev);
-      pending = false;
-    }
+    tile(need_mask, kst, vprev, k0);
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct loads landed
-    __syncthreads();
+    // Tile kt+1 must have landed (this wave's share); tiles kt+2 .. kt+PF may
+    // still be in flight.
+    // Tile kt+1 has landed once at most PF-1 tiles' loads are outstanding.
+    // Every LDS read of this tile was consumed by an MFMA above, so after the
+    // barrier the stages read here may be overwritten.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
+    __builtin_amdgcn_s_barrier();
   }
-  if (pending) flush((kt_end - 1 - kt_begin) % 3);
+  // The last tile's PV products.
+  rescale();
+  if (kt_begin < kt_end) o_phase((kt_end - 1 - kt_begin) % NVST);
 
   // Epilogue: one division per row, RNE to the element type, natural-log LSE.
 #pragma unroll
@@ -432,21 +520,31 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   }
 }
 
+#ifndef FA_BC64
+#define FA_BC64 64
+#endif
 #ifndef FA_BC128
-#define FA_BC128 64
+#define FA_BC128 32
+#endif
+#ifndef FA_BC256
+#define FA_BC256 32
+#endif
+#ifndef FA_PF
+#define FA_PF 2
 #endif
 template <class Ty, int D, int MASK>
 struct Instance {
   static constexpr int NW = 4;
-  static constexpr int BC = D == 128 ? FA_BC128 : 64;
+  static constexpr int BC = D == 64 ? FA_BC64 : D == 128 ? FA_BC128 : FA_BC256;
   static constexpr int NH = D <= 128 ? 2 : 1;
+  static constexpr int PF = D == 256 && FA_PF > 3 ? 3 : FA_PF;  // LDS budget
   static constexpr int BR = 32 * NH * NW;
   static bool run(const FwdArgs *a, hipStream_t stream, bool launch, LaunchInfo *info,
                   hipError_t *err) {
     static char name[96];
     static const char *mk[3] = {"none", "causal", "window"};
-    snprintf(name, sizeof(name), "fa_fwd_mfma<%s,d%d,%s,br%d,bc%d>", Ty::kName, D, mk[MASK],
-             BR, BC);
+    snprintf(name, sizeof(name), "fa_fwd_mfma<%s,d%d,%s,br%d,bc%d,pf%d>", Ty::kName, D,
+             mk[MASK], BR, BC, PF);
     info->name = name;
     info->block_rows = BR;
     info->threads = NW * 64;
@@ -456,7 +554,7 @@ struct Instance {
     const dim3 block(NW * 64);
     FwdArgs args = *a;
     void *kargs[] = {&args};
-    *err = hipLaunchKernel((const void *)&fa_fwd_mfma_kernel<Ty, D, MASK, NW, BC, NH>, grid,
+    *err = hipLaunchKernel((const void *)&fa_fwd_mfma_kernel<Ty, D, MASK, NW, BC, NH, PF>, grid,
                            block, kargs, 0, stream);
     return true;
   }
