@@ -23,10 +23,13 @@ ARCH = "gfx950"
 
 SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_f32.hip"]
 
-# Per-source extra flags.  The matrix-core kernel never produces or consumes
-# NaN (masked scores are -inf, which stays honoured), so NaN-quieting of
-# min/max operands is dropped there.
-EXTRA_FLAGS = {"fa_fwd_mfma.hip": ["-fno-honor-nans"]}
+# Per-source extra flags for the matrix-core kernel:
+#  * it never produces or consumes NaN (masked scores are -inf, which stays
+#    honoured), so NaN-quieting of min/max operands is dropped;
+#  * MFMA results (scores, output accumulators) are kept in VGPRs, where the
+#    softmax and the rescale use them, instead of AGPRs that would need a
+#    copy for every vector-ALU access.
+EXTRA_FLAGS = {"fa_fwd_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -277,12 +277,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     l[h] = 0.f;        // this lane's share of the running denominator
     alpha[h] = 1.f;
   }
-  // O accumulators live in AGPRs (MFMA accumulates there directly); only the
-  // rare rescale and the epilogue read them back.
-#pragma unroll
-  for (int h = 0; h < NH; ++h)
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) asm volatile("" : "+a"(oacc[h][i]));
+  // O accumulators and scores stay in VGPRs (the file is built with the
+  // VGPR-destination MFMA form): the softmax and the rare rescale then read
+  // them directly, without AGPR copies.
   // The PV products lag one tile: pk / alpha hold the previous tile's
   // weights and factors until the next tile (or the epilogue) multiplies them
   // in.  Initially the weights are zero, and so is the V stage they meet.
@@ -388,16 +385,25 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     }
   };
 
-  // Online-softmax update of half h from its raw scores: new packed weights
-  // in pk_new, accumulator factor in alpha[h].
-  auto softmax = [&](int h, u32x4 (&pk_new)[NPS]) __attribute__((always_inline)) {
+  // Online softmax, in pieces that the pipeline below places next to MFMA work.
+  // head(h): row maximum of half h's raw scores, new offset and factor.
+  // exps(h, kk0, kk1): weights of steps [kk0, kk1) against that offset,
+  //   packed for the PV product, with their fp32 sum kept in lpart[h].
+  // finish(h): l <- l * alpha + lpart.
+  float m_use[NH], lpart[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    m_use[h] = 0.f;
+    lpart[h] = -0.f;
+  }
+  auto sm_head = [&](int h, const f32x16 (&sc)[NKB]) __attribute__((always_inline)) {
     float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 4)
-        t4[r >> 2] = fmaxf(t4[r >> 2], fmaxf(fmaxf(sacc[h][kb][r], sacc[h][kb][r + 1]),
-                                             fmaxf(sacc[h][kb][r + 2], sacc[h][kb][r + 3])));
+        t4[r >> 2] = fmaxf(t4[r >> 2], fmaxf(fmaxf(sc[kb][r], sc[kb][r + 1]),
+                                             fmaxf(sc[kb][r + 2], sc[kb][r + 3])));
     float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
     const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, tmax),
                                                      __builtin_bit_cast(uint32_t, tmax),
@@ -406,46 +412,75 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
                  __builtin_bit_cast(float, (uint32_t)sw[1])) * c;  // c > 0 keeps order
     const float m_old = m[h];
     const float m_new = tmax > m_old + TAU ? tmax : m_old;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // row fully masked so far
-    alpha[h] = __builtin_amdgcn_exp2f(m_old - m_use);      // 1 if unchanged, 0 from -inf
+    m_use[h] = m_new == -INFINITY ? 0.f : m_new;          // row fully masked so far
+    alpha[h] = __builtin_amdgcn_exp2f(m_old - m_use[h]);  // 1 if unchanged, 0 from -inf
     m[h] = m_new;
+    lpart[h] = -0.f;
+  };
+  auto sm_exps = [&](int h, const f32x16 (&sc)[NKB], u32x4 (&pk_out)[NPS], int kk0, int kk1)
+                     __attribute__((always_inline)) {
     float s4[4] = {-0.f, -0.f, -0.f, -0.f};  // -0 + x == x folds away
 #pragma unroll
-    for (int kk = 0; kk < NPS; ++kk) {
+    for (int kk = kk0; kk < kk1; ++kk) {
       const int kb = kk >> 1, base = 8 * (kk & 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[h][kb][base + 2 * j], c, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[h][kb][base + 2 * j + 1], c, -m_use));
-        pk_new[kk][j] = Ty::pack2(p0, p1);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][base + 2 * j], c, -m_use[h]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][base + 2 * j + 1], c, -m_use[h]));
+        pk_out[kk][j] = Ty::pack2(p0, p1);
         s4[j] += p0 + p1;
       }
     }
-    l[h] = l[h] * alpha[h] + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
+    lpart[h] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  };
+  auto sm_finish = [&](int h) __attribute__((always_inline)) {
+    l[h] = l[h] * alpha[h] + lpart[h];
   };
 
-  // One key tile.  Phase A: S for every half, each K operand read once and
-  // used by all halves.  Phase B: the previous tile's PV products (each V
-  // operand read once), independent of this tile's softmaxes, which issue
-  // next to them.
+  // Software pipeline over key tiles (t = current tile):
+  //   phase A: S(t) = K_t Q^T on MFMA, next to the second softmax piece of
+  //            tile t-1 (half 1 when a wave has two halves, the second half
+  //            of the keys otherwise);
+  //   phase B: O += V_{t-1}^T P(t-1)^T on MFMA (both halves share each V
+  //            operand), next to the first softmax piece of tile t.
+  // Every piece is independent of the MFMAs it issues beside, so the vector
+  // ALU and the matrix core work at the same time inside one wave.  The
+  // leftover pieces of the last tile run after the loop.
+  constexpr int SPLIT = NH == 2 ? NPS : NPS / 2;  // steps done in phase B (NH == 1)
+  f32x16 sprev[NKB];  // scores of tile t-1 still awaiting their second piece
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sprev[kb][r] = -INFINITY;
+
+  auto second_piece = [&]() __attribute__((always_inline)) {
+    if (NH == 2) {
+      sm_head(1, sprev);
+      sm_exps(1, sprev, pk[1], 0, NPS);
+      sm_finish(1);
+    } else {
+      sm_exps(0, sprev, pk[0], SPLIT, NPS);
+      sm_finish(0);
+    }
+  };
+
   auto tile = [&](bool masked, int kst, int vprev, int k0) __attribute__((always_inline)) {
     s_phase(kst);
+    second_piece();
     if (masked) apply_mask(k0);
-    rescale();  // factors of the pending tile
-    u32x4 pk_new[NH][NPS];
-    o_phase(vprev);  // zero weights when nothing is pending
+    rescale();  // factors of tile t-1, now complete
+    o_phase(vprev);
+    // first piece of tile t: half 0 (or the first keys of the only half)
+    u32x4 pk0_new[NPS];
 #pragma unroll
-    for (int h = 0; h < NH; ++h) softmax(h, pk_new[h]);
-    // Interleave: per V operand, its two transposing reads, its NH MFMAs and
-    // a share of the softmax's vector instructions.
+    for (int i = 0; i < NPS; ++i) pk0_new[i] = pk[0][i];
+    sm_head(0, sacc[0]);
+    sm_exps(0, sacc[0], pk0_new, 0, SPLIT);
+    if (NH == 2) sm_finish(0);
 #pragma unroll
-    for (int i = 0; i < NPS * NDB; ++i) {
-      (void)0;
-    }
+    for (int i = 0; i < NPS; ++i) pk[0][i] = pk0_new[i];
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int i = 0; i < NPS; ++i) pk[h][i] = pk_new[h][i];
+    for (int kb = 0; kb < NKB; ++kb) sprev[kb] = sacc[NH - 1][kb];
   };
 
   // Zero the V stage that the first tile's (empty) pending product reads, so
@@ -491,7 +526,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
     __builtin_amdgcn_s_barrier();
   }
-  // The last tile's PV products.
+  // The last tile: its second softmax piece, then its PV products.
+  second_piece();
   rescale();
   if (kt_begin < kt_end) o_phase((kt_end - 1 - kt_begin) % NVST);
 
