@@ -23,7 +23,7 @@
 //   * Q^T (the B operand) is loaded once into VGPRs;
 //   * K and V tiles go from HBM straight into LDS with 16-byte-per-lane
 //     direct buffer loads (no VGPR staging); both are stored row-major
-//     [key][d] with a 16-byte-chunk XOR swizzle (chunk ^ (key & 7)), chosen
+//     [key][d] with a 16-byte-chunk XOR swizzle (see swz below), chosen
 //     through each lane's global offset, so that the operand reads below are
 //     free of bank conflicts;
 //   * the K operand of S^T is one ds_read_b128 per lane; the V^T operand of
@@ -161,13 +161,23 @@ __device__ inline bool key_visible(int key, int row, int S, int window) {
 }
 
 // 16-byte chunk position of chunk c in LDS row r (64 banks of 4 bytes: a
-// 256-byte bank line).  Rows of at least 256 bytes XOR the chunk with the low
-// four row bits; 128-byte rows (d = 64) share a bank line in pairs and XOR
-// with the next three bits.  Either way, 16 consecutive rows reading the same
-// logical chunk hit 16 different 16-byte bank groups.
+// 256-byte bank line).  The chunk is XORed with f(r), which has two jobs:
+//   * 16 consecutive rows reading the same logical chunk (the K operand, one
+//     ds_read_b128 per lane, 16 lanes per LDS cycle) must land in 16
+//     different 16-byte bank groups, so f must be a bijection on 16
+//     consecutive rows (on 8 row pairs for d = 64, whose 128-byte rows share
+//     a bank line in pairs);
+//   * the transposing V reads fetch 4 consecutive keys x 4 consecutive chunks
+//     per half wave, so the 4 keys must also differ in the chunk bits above
+//     the lowest two, which a plain XOR with the low row bits does not give
+//     (it only permutes chunks within groups of four).
+// Hence the low row bits go to the high chunk bits: f = 4*(r&3) + (r>>2 & 3)
+// for rows of at least 256 bytes; for d = 64 the same rotation applied to the
+// row-pair index (r>>1) & 7.
 template <int D>
 __device__ __host__ constexpr int swz(int r, int c) {
-  return D >= 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+  return D >= 128 ? (c ^ (4 * (r & 3) + ((r >> 2) & 3)))
+                  : (c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3)));
 }
 
 template <class Ty, int D, int MASK, int NW, int BC, int NH, int PF>
@@ -296,23 +306,22 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // V^T operand of step kk, d block db, part i2: lane (group G = lane/16,
   // n = lane%16) names row key = 16*kk + 8*i2 + tr_key (tr_key = 4*lg + n/4)
   // at column d = 32*db + 16*(G&1) + 4*(n&3) and receives keys
-  // 16*kk + 8*i2 + 4*lg + 0..3 of column 32*db + lane%32.  With t = (d/8) % 4
-  // the swizzled chunk splits into a lane part (one base per parity of db for
-  // d >= 128) and a constant.
-  const int tr_key = 4 * lg + ((lane & 15) >> 2);
-  const int tr_t = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int tr_lane = tr_key * (D * 2) + 8 * (lane & 1);
-  int v_base[2];
-  if (D >= 128) {
-    v_base[0] = tr_lane + 16 * (tr_t ^ (tr_key & 3)) + 64 * lg;
-    v_base[1] = tr_lane + 16 * (tr_t ^ (tr_key & 3)) + 64 * (1 - lg);
-  } else {
-    v_base[0] = v_base[1] = tr_lane + 16 * (tr_t ^ (tr_key >> 1));
+  // 16*kk + 8*i2 + 4*lg + 0..3 of column 32*db + lane%32.  The swizzle
+  // depends on the row only through its low four bits and leaves chunk bits
+  // above the fourth alone, so the offset is a lane base chosen by (i2, the
+  // low two bits of db) plus the constant 16*kk rows and 16*(db & ~3) chunks.
+  constexpr int NVB = D >= 128 ? 8 : 4;
+  int v_base[NVB];
+  {
+    const int tr_key = 4 * lg + ((lane & 15) >> 2);
+    const int tr_c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int j = 0; j < NVB; ++j) {
+      const int key = 8 * (j & 1) + tr_key;
+      v_base[j] = key * (D * 2) + 16 * swz<D>(key, 4 * (j >> 1) + tr_c) + 8 * (lane & 1);
+    }
   }
-  auto v_const = [](int kk, int i2, int db) constexpr {
-    return D >= 128 ? (16 * kk + 8 * i2) * (D * 2) + 256 * (db >> 2) + 128 * (((db >> 1) & 1) ^ i2)
-                    : (16 * kk + 8 * i2) * (D * 2) + 64 * (db ^ i2);
-  };
+  auto v_off = [](int kk, int db) constexpr { return 16 * kk * (D * 2) + 64 * (db & ~3); };
 
   auto s_phase = [&](int kst) __attribute__((always_inline)) {
     const char *kl = (const char *)&k_lds[kst][0];
@@ -342,7 +351,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // O_h^T += V^T P_h^T for every half, each V operand read once.
   auto o_phase = [&](int vst) __attribute__((always_inline)) {
     const char *vl = (const char *)&v_lds[vst][0];
-    const char *vp[2] = {vl + v_base[0], vl + v_base[1]};
+    const char *vp[NVB];
+#pragma unroll
+    for (int j = 0; j < NVB; ++j) vp[j] = vl + v_base[j];
 #pragma unroll
     for (int kk = 0; kk < NPS; ++kk)
 #pragma unroll
@@ -351,7 +362,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
           const u32x2 v2 =
-              lds_read_tr16((const FA_LDS void *)(vp[db & 1] + v_const(kk, i2, db)));
+              lds_read_tr16((const FA_LDS void *)(vp[2 * (db & 3) + i2] + v_off(kk, db)));
           op[2 * i2] = v2[0];
           op[2 * i2 + 1] = v2[1];
         }
