@@ -77,7 +77,13 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr float TAU = 8.0f;  // max growth (base 2) tolerated before rescaling
+constexpr float TAU = 8.0f;
+#ifndef FA_VALU_A
+#define FA_VALU_A 3
+#endif
+#ifndef FA_VALU_B
+#define FA_VALU_B 5
+#endif  // max growth (base 2) tolerated before rescaling
 
 struct TBF16 {
   static constexpr const char *kName = "bf16";
@@ -148,6 +154,12 @@ __device__ inline u32x2 lds_read_tr16(const FA_LDS void *p) {
   return __builtin_bit_cast(
       u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4 *)const_cast<FA_LDS void *>(p)));
 }
+
+// An empty use that keeps a value's computation in the code region where it
+// is written (the compiler would otherwise sink ALU work past later branches,
+// away from the MFMAs it is meant to run beside).
+__device__ inline void pin(float x) { asm volatile("" ::"v"(x)); }
+__device__ inline void pin(uint32_t x) { asm volatile("" ::"v"(x)); }
 
 __device__ inline float wave_partner(float x) {  // value held by lane ^ 32
   return __shfl_xor(x, 32, 64);
@@ -323,54 +335,39 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   }
   auto v_off = [](int kk, int db) constexpr { return 16 * kk * (D * 2) + 64 * (db & ~3); };
 
-  auto s_phase = [&](int kst) __attribute__((always_inline)) {
-    const char *kl = (const char *)&k_lds[kst][0];
-    const char *kp[KSW];
-#pragma unroll
-    for (int j = 0; j < KSW; ++j) kp[j] = kl + k_base[j];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[h][kb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 op =
-            *(const u32x4 *)(kp[ks % KSW] + kb * (32 * D * 2) + 16 * 2 * KSW * (ks / KSW));
-#pragma unroll
-        for (int h = 0; h < NH; ++h) sacc[h][kb] = Ty::mfma(op, qreg[h][ks], sacc[h][kb]);
-      }
-    // scores go to the vector ALU next: keep them in VGPRs
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) asm volatile("" : "+v"(sacc[h][kb]));
+  // K operand of score step st = (ks, kb): 16 bytes per lane.
+  auto read_k = [&](const char *kl, int st) __attribute__((always_inline)) {
+    const int ks = st / NKB, kb = st % NKB;
+    return *(const u32x4 *)(kl + k_base[ks % KSW] + kb * (32 * D * 2) + 16 * 2 * KSW * (ks / KSW));
   };
-
-  // O_h^T += V^T P_h^T for every half, each V operand read once.
+  // V^T operand of product step st = (kk, db): two transposing reads.
+  auto read_v = [&](const char *vl, int st) __attribute__((always_inline)) {
+    const int kk = st / NDB, db = st % NDB;
+    u32x4 op;
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const u32x2 v2 = lds_read_tr16(
+          (const FA_LDS void *)(vl + v_base[2 * (db & 3) + i2] + v_off(kk, db)));
+      op[2 * i2] = v2[0];
+      op[2 * i2 + 1] = v2[1];
+    }
+    return op;
+  };
+  // O_h^T += V^T P_h^T for every half, without interleaved work (last tile).
   auto o_phase = [&](int vst) __attribute__((always_inline)) {
     const char *vl = (const char *)&v_lds[vst][0];
-    const char *vp[NVB];
 #pragma unroll
-    for (int j = 0; j < NVB; ++j) vp[j] = vl + v_base[j];
+    for (int st = 0; st < NPS * NDB; ++st) {
+      const u32x4 op = read_v(vl, st);
 #pragma unroll
-    for (int kk = 0; kk < NPS; ++kk)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        u32x4 op;
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const u32x2 v2 =
-              lds_read_tr16((const FA_LDS void *)(vp[2 * (db & 3) + i2] + v_off(kk, db)));
-          op[2 * i2] = v2[0];
-          op[2 * i2 + 1] = v2[1];
-        }
-#pragma unroll
-        for (int h = 0; h < NH; ++h) oacc[h][db] = Ty::mfma(op, pk[h][kk], oacc[h][db]);
-      }
+      for (int h = 0; h < NH; ++h)
+        oacc[h][st % NDB] = Ty::mfma(op, pk[h][st / NDB], oacc[h][st % NDB]);
+    }
   };
 
+  // O_h *= alpha_h where some lane's factor differs from 1.  Rare once the
+  // running maxima settle (see TAU), so it sits at the end of a tile, where
+  // its branch does not split the MFMA/ALU interleaving of the phases.
   auto rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -398,100 +395,187 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 
   // Online softmax, in pieces that the pipeline below places next to MFMA work.
   // head(h): row maximum of half h's raw scores, new offset and factor.
-  // exps(h, kk0, kk1): weights of steps [kk0, kk1) against that offset,
-  //   packed for the PV product, with their fp32 sum kept in lpart[h].
-  // finish(h): l <- l * alpha + lpart.
+  // Contraction step kk of the PV product covers, in each lane, the 8 scores
+  // sc[kk/2][8*(kk%2) .. +7]; weights are exp2(c*s - offset).
+  // finish(h): l <- l * alpha + (sum of the tile's weights).
   float m_use[NH], lpart[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     m_use[h] = 0.f;
     lpart[h] = -0.f;
   }
-  auto sm_head = [&](int h, const f32x16 (&sc)[NKB]) __attribute__((always_inline)) {
-    float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 4)
-        t4[r >> 2] = fmaxf(t4[r >> 2], fmaxf(fmaxf(sc[kb][r], sc[kb][r + 1]),
-                                             fmaxf(sc[kb][r + 2], sc[kb][r + 3])));
-    float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
-    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, tmax),
-                                                     __builtin_bit_cast(uint32_t, tmax),
-                                                     false, false);
-    tmax = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
-                 __builtin_bit_cast(float, (uint32_t)sw[1])) * c;  // c > 0 keeps order
-    const float m_old = m[h];
-    const float m_new = tmax > m_old + TAU ? tmax : m_old;
-    m_use[h] = m_new == -INFINITY ? 0.f : m_new;          // row fully masked so far
-    alpha[h] = __builtin_amdgcn_exp2f(m_old - m_use[h]);  // 1 if unchanged, 0 from -inf
-    m[h] = m_new;
-    lpart[h] = -0.f;
-  };
-  auto sm_exps = [&](int h, const f32x16 (&sc)[NKB], u32x4 (&pk_out)[NPS], int kk0, int kk1)
-                     __attribute__((always_inline)) {
-    float s4[4] = {-0.f, -0.f, -0.f, -0.f};  // -0 + x == x folds away
-#pragma unroll
-    for (int kk = kk0; kk < kk1; ++kk) {
-      const int kb = kk >> 1, base = 8 * (kk & 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][base + 2 * j], c, -m_use[h]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][base + 2 * j + 1], c, -m_use[h]));
-        pk_out[kk][j] = Ty::pack2(p0, p1);
-        s4[j] += p0 + p1;
-      }
-    }
-    lpart[h] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
-  };
   auto sm_finish = [&](int h) __attribute__((always_inline)) {
     l[h] = l[h] * alpha[h] + lpart[h];
   };
 
   // Software pipeline over key tiles (t = current tile):
-  //   phase A: S(t) = K_t Q^T on MFMA, next to the second softmax piece of
-  //            tile t-1 (half 1 when a wave has two halves, the second half
-  //            of the keys otherwise);
+  //   phase A: S(t) = K_t Q^T on MFMA, next to the exponentials of tile t-1:
+  //            weights from the exponent arguments saved by phase B of t-1,
+  //            packed for the PV product, and the denominators' update;
   //   phase B: O += V_{t-1}^T P(t-1)^T on MFMA (both halves share each V
-  //            operand), next to the first softmax piece of tile t.
-  // Every piece is independent of the MFMAs it issues beside, so the vector
-  // ALU and the matrix core work at the same time inside one wave.  The
-  // leftover pieces of the last tile run after the loop.
-  constexpr int SPLIT = NH == 2 ? NPS : NPS / 2;  // steps done in phase B (NH == 1)
-  f32x16 sprev[NKB];  // scores of tile t-1 still awaiting their second piece
+  //            operand), next to the rest of tile t's softmax: row maxima,
+  //            offsets and factors of every half, and the exponent arguments
+  //            c*s - offset of every score;
+  //   then the rare rescale of O by tile t's factors, which must land after
+  //   the products of tile t-1 and before those of tile t.
+  // Each phase is one basic block whose ALU work is independent of the MFMAs
+  // it issues beside, so the vector ALU and the matrix core work at the same
+  // time inside one wave, and the two phases carry similar ALU loads.  Only
+  // exponent arguments cross from one tile to the next, so no score
+  // registers are copied along the loop.
+  float xdef[NH][NPS][8];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
+  for (int h = 0; h < NH; ++h)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sprev[kb][r] = -INFINITY;
+    for (int i = 0; i < NPS; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xdef[h][i][j] = -INFINITY;
 
-  auto second_piece = [&]() __attribute__((always_inline)) {
-    if (NH == 2) {
-      sm_head(1, sprev);
-      sm_exps(1, sprev, pk[1], 0, NPS);
-      sm_finish(1);
-    } else {
-      sm_exps(0, sprev, pk[0], SPLIT, NPS);
-      sm_finish(0);
+  // Phase A work, in units: unit u makes the weights of pair j = u % 4 of
+  // step kk = (u / 4) % NPS of half h = u / (4 * NPS) from the saved
+  // exponent arguments; a_finish folds the sums into the denominators.
+  constexpr int UA = NH * NPS * 4;
+  float s4a[NH][4];
+  auto a_start = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s4a[h][j] = -0.f;  // -0 + x == x folds away
+  };
+  auto a_unit = [&](int u) __attribute__((always_inline)) {
+    const int h = u / (4 * NPS), kk = (u / 4) % NPS, j = u % 4;
+    const float p0 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j]);
+    const float p1 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j + 1]);
+    pk[h][kk][j] = Ty::pack2(p0, p1);
+    s4a[h][j] += p0 + p1;
+    pin(pk[h][kk][j]);
+    pin(s4a[h][j]);
+  };
+  auto a_finish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      lpart[h] = (s4a[h][0] + s4a[h][1]) + (s4a[h][2] + s4a[h][3]);
+      sm_finish(h);
+      pin(l[h]);
     }
   };
 
-  auto tile = [&](bool masked, int kst, int vprev, int k0) __attribute__((always_inline)) {
-    s_phase(kst);
-    second_piece();
-    if (masked) apply_mask(k0);
-    rescale();  // factors of tile t-1, now complete
-    o_phase(vprev);
-    // first piece of tile t: half 0 (or the first keys of the only half)
-    u32x4 pk0_new[NPS];
+  // Phase B work, in units: 4 * NH partial row maxima (quarter q of half h),
+  // NH head finishes (exchange with lane ^ 32, new offset and factor), then
+  // 2 * NPS * NH groups of four exponent arguments.
+  constexpr int UB_MAX = 4 * NH, UB_FIN = NH, UB_ARG = 2 * NPS * NH;
+  constexpr int UB = UB_MAX + UB_FIN + UB_ARG;
+  float t4b[NH][4];
+  auto b_unit = [&](int u) __attribute__((always_inline)) {
+    if (u < UB_MAX) {
+      const int h = u / 4, q = u % 4;
+      float t = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NPS; ++i) pk0_new[i] = pk[0][i];
-    sm_head(0, sacc[0]);
-    sm_exps(0, sacc[0], pk0_new, 0, SPLIT);
-    if (NH == 2) sm_finish(0);
+      for (int kb = 0; kb < NKB; ++kb)
+        t = fmaxf(t, fmaxf(fmaxf(sacc[h][kb][4 * q], sacc[h][kb][4 * q + 1]),
+                           fmaxf(sacc[h][kb][4 * q + 2], sacc[h][kb][4 * q + 3])));
+      t4b[h][q] = t;
+      pin(t4b[h][q]);
+    } else if (u < UB_MAX + UB_FIN) {
+      const int h = u - UB_MAX;
+      float tmax = fmaxf(fmaxf(t4b[h][0], t4b[h][1]), fmaxf(t4b[h][2], t4b[h][3]));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, tmax),
+                                                       __builtin_bit_cast(uint32_t, tmax),
+                                                       false, false);
+      tmax = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
+                   __builtin_bit_cast(float, (uint32_t)sw[1])) * c;  // c > 0 keeps order
+      const float m_old = m[h];
+      const float m_new = tmax > m_old + TAU ? tmax : m_old;
+      m_use[h] = m_new == -INFINITY ? 0.f : m_new;          // row fully masked so far
+      alpha[h] = __builtin_amdgcn_exp2f(m_old - m_use[h]);  // 1 if unchanged, 0 from -inf
+      m[h] = m_new;
+      pin(m_use[h]);
+      pin(alpha[h]);
+    } else {
+      const int v = u - UB_MAX - UB_FIN;
+      const int h = v / (2 * NPS), kk = (v / 2) % NPS, part = v % 2;
+      const int kb = kk >> 1, base = 8 * (kk & 1) + 4 * part;
 #pragma unroll
-    for (int i = 0; i < NPS; ++i) pk[0][i] = pk0_new[i];
+      for (int i = 0; i < 4; ++i) {
+        xdef[h][kk][4 * part + i] = fmaf(sacc[h][kb][base + i], c, -m_use[h]);
+        pin(xdef[h][kk][4 * part + i]);
+      }
+    }
+  };
+
+  // One tile, software-pipelined (t = this tile):
+  //   phase A: S(t) = K_t Q^T on MFMA, next to the weights of tile t-1
+  //            (phase A units), the denominators' update and the direct
+  //            loads of tile t+PF;
+  //   phase B: O += V_{t-1}^T P(t-1)^T on MFMA, next to the softmax head of
+  //            tile t (phase B units): row maxima, offsets, factors and the
+  //            exponent arguments c*s - offset of every score;
+  //   then the rare rescale of O by tile t's factors, which must land after
+  //   the products of tile t-1 and before those of tile t.
+  // Both phases are written as a sequence of steps (operand read one step
+  // ahead, one MFMA, its share of the ALU units) separated by scheduling
+  // fences, so the instruction stream alternates matrix and vector work in
+  // this order: the matrix core runs each MFMA while the wave issues the ALU
+  // work behind it.  Only exponent arguments cross from one tile to the
+  // next, so no score registers are copied along the loop.
+  constexpr int NSA = NKS * NKB, MA = NSA * NH;  // score steps, MFMAs
+  constexpr int NSB = NPS * NDB, MB = NSB * NH;  // product steps, MFMAs
+  constexpr int NDMA = 2 * LOADS_PER_WAVE;       // direct loads per tile
+  auto tile = [&](auto masked_c, int kst, int vprev, int k0, int lkt, int lks, int lvs)
+                  __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked_c)::value;
+    const char *kl = (const char *)&k_lds[kst][0];
+    const char *vl = (const char *)&v_lds[vprev][0];
+    const int lk0 = lkt * BC;
+    // ---- phase A ----
+    a_start();
+    u32x4 kop[2];
+    kop[0] = read_k(kl, 0);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sprev[kb] = sacc[NH - 1][kb];
+    for (int st = 0; st < NSA; ++st) {
+      if (st + 1 < NSA) kop[(st + 1) & 1] = read_k(kl, st + 1);
+      const int ks = st / NKB, kb = st % NKB;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int mi = st * NH + h;
+        sacc[h][kb] = Ty::mfma(kop[st & 1], qreg[h][ks], ks == 0 ? f32x16{} : sacc[h][kb]);
+#pragma unroll
+        for (int u = mi * UA / MA; u < (mi + 1) * UA / MA; ++u) a_unit(u);
+        // direct loads of tile t+PF, one after each of the MFMAs 1, 3, 5, ...
+        if (mi % 2 == 1 && mi / 2 < NDMA) {
+          const int d = mi / 2, i = d >> 1;
+          const int blk = wave * LOADS_PER_WAVE + i;
+          const int pos = 64 * blk + lane;
+          const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
+          const uint32_t off = (uint32_t)((lk0 + r) * D + 8 * cc) * 2u;
+          if (d & 1)
+            load16_to_lds(rv, off, (uint32_t)(uintptr_t)&v_lds[lvs][64 * blk]);
+          else
+            load16_to_lds(rk, off, (uint32_t)(uintptr_t)&k_lds[lks][64 * blk]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    a_finish();
+    u32x4 vop[2];
+    vop[0] = read_v(vl, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- phase B ----
+    if (kMasked) apply_mask(k0);
+#pragma unroll
+    for (int st = 0; st < NSB; ++st) {
+      if (st + 1 < NSB) vop[(st + 1) & 1] = read_v(vl, st + 1);
+      const int kk = st / NDB, db = st % NDB;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int mi = st * NH + h;
+        oacc[h][db] = Ty::mfma(vop[st & 1], pk[h][kk], oacc[h][db]);
+#pragma unroll
+        for (int u = mi * UB / MB; u < (mi + 1) * UB / MB; ++u) b_unit(u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    rescale();  // tile t's factors, after the products of tile t-1
   };
 
   // Zero the V stage that the first tile's (empty) pending product reads, so
@@ -510,36 +594,45 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
   __builtin_amdgcn_s_barrier();
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int it = kt - kt_begin;
-    const int kst = it % NKST, vprev = (it + NVST - 1) % NVST;
-    load_tile(tile_or_none(kt + PF), (it + PF) % NKST, (it + PF) % NVST);
-
-    // Every wave runs every tile of the work-group's range; a tile that lies
-    // outside a wave's band is simply fully masked (weights 0, factor 1).
-    // That costs a few percent of MFMA work on band edges but keeps a single
-    // copy of each phase in the loop.
-    const int k0 = kt * BC;
-    bool need_mask;
-    if (MASK == kMaskCausal)
-      need_mask = k0 + BC - 1 > wr0;
-    else if (MASK == kMaskWindow)
-      need_mask = k0 + BC - 1 > wr0 || k0 <= wr1 - a.window;
-    else
-      need_mask = k0 + BC > S;
-    tile(need_mask, kst, vprev, k0);
-
-    // Tile kt+1 must have landed (this wave's share); tiles kt+2 .. kt+PF may
-    // still be in flight.
-    // Tile kt+1 has landed once at most PF-1 tiles' loads are outstanding.
-    // Every LDS read of this tile was consumed by an MFMA above, so after the
-    // barrier the stages read here may be overwritten.
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
-    __builtin_amdgcn_s_barrier();
+  auto run_tiles = [&](auto masked_c, int kt_from, int kt_to) __attribute__((always_inline)) {
+    for (int kt = kt_from; kt < kt_to; ++kt) {
+      const int it = kt - kt_begin;
+      const int kst = it % NKST, vprev = (it + NVST - 1) % NVST;
+      tile(masked_c, kst, vprev, kt * BC, tile_or_none(kt + PF), (it + PF) % NKST,
+           (it + PF) % NVST);
+      // Tile kt+1 has landed (this wave's share) once at most PF-1 tiles'
+      // loads are outstanding; the barrier extends that to the whole
+      // work-group.  Every LDS read of this tile was consumed by an MFMA
+      // above, so after the barrier the stages read here may be overwritten.
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
+      __builtin_amdgcn_s_barrier();
+    }
+  };
+  // Every wave runs every tile of the work-group's range (the loads and
+  // barriers are shared); per wave, the range splits into a masked run at the
+  // window's lower edge, a plain run, and a masked run from the first tile
+  // that reaches past the wave's first row (or the sequence end).  A tile
+  // outside a wave's band is simply fully masked (weights 0, factor 1).
+  // Separate loops rather than a branch between two tile bodies keep the
+  // register allocation of the two copies apart.
+  int plain_begin = kt_begin, plain_end;
+  if (MASK == kMaskNone) {
+    plain_end = S / BC;  // a ragged last tile is masked
+  } else {
+    plain_end = (wr0 + 1) / BC;  // tiles with k0 + BC - 1 <= wr0 need no diagonal mask
+    if (MASK == kMaskWindow && wr1 - a.window >= 0)
+      plain_begin = (wr1 - a.window) / BC + 1;  // tiles with k0 <= wr1 - window are cut
   }
-  // The last tile: its second softmax piece, then its PV products.
-  second_piece();
-  rescale();
+  plain_begin = min(max(plain_begin, kt_begin), kt_end);
+  plain_end = min(max(plain_end, plain_begin), kt_end);
+  if (MASK == kMaskWindow) run_tiles(std::true_type{}, kt_begin, plain_begin);
+  run_tiles(std::false_type{}, plain_begin, plain_end);
+  run_tiles(std::true_type{}, plain_end, kt_end);
+  // The last tile: its weights, then its PV products.
+  a_start();
+#pragma unroll
+  for (int u = 0; u < UA; ++u) a_unit(u);
+  a_finish();
   if (kt_begin < kt_end) o_phase((kt_end - 1 - kt_begin) % NVST);
 
   // Epilogue: one division per row, RNE to the element type, natural-log LSE.
