@@ -78,11 +78,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float TAU = 8.0f;
-#ifndef FA_VALU_A
-#define FA_VALU_A 3
-#endif
-#ifndef FA_VALU_B
-#define FA_VALU_B 5
+#ifndef FA_RPD
+#define FA_RPD 3
 #endif  // max growth (base 2) tolerated before rescaling
 
 struct TBF16 {
@@ -521,6 +518,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   constexpr int NSA = NKS * NKB, MA = NSA * NH;  // score steps, MFMAs
   constexpr int NSB = NPS * NDB, MB = NSB * NH;  // product steps, MFMAs
   constexpr int NDMA = 2 * LOADS_PER_WAVE;       // direct loads per tile
+  constexpr int RPD = FA_RPD;                    // operand reads run RPD steps ahead
   auto tile = [&](auto masked_c, int kst, int vprev, int k0, int lkt, int lks, int lvs)
                   __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked_c)::value;
@@ -529,16 +527,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     const int lk0 = lkt * BC;
     // ---- phase A ----
     a_start();
-    u32x4 kop[2];
-    kop[0] = read_k(kl, 0);
+    u32x4 kop[RPD + 1];
+#pragma unroll
+    for (int st = 0; st < RPD && st < NSA; ++st) kop[st] = read_k(kl, st);
 #pragma unroll
     for (int st = 0; st < NSA; ++st) {
-      if (st + 1 < NSA) kop[(st + 1) & 1] = read_k(kl, st + 1);
+      if (st + RPD < NSA) kop[(st + RPD) % (RPD + 1)] = read_k(kl, st + RPD);
       const int ks = st / NKB, kb = st % NKB;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         const int mi = st * NH + h;
-        sacc[h][kb] = Ty::mfma(kop[st & 1], qreg[h][ks], ks == 0 ? f32x16{} : sacc[h][kb]);
+        sacc[h][kb] = Ty::mfma(kop[st % (RPD + 1)], qreg[h][ks], ks == 0 ? f32x16{} : sacc[h][kb]);
 #pragma unroll
         for (int u = mi * UA / MA; u < (mi + 1) * UA / MA; ++u) a_unit(u);
         // direct loads of tile t+PF, one after each of the MFMAs 1, 3, 5, ...
@@ -557,19 +556,20 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       }
     }
     a_finish();
-    u32x4 vop[2];
-    vop[0] = read_v(vl, 0);
+    u32x4 vop[RPD + 1];
+#pragma unroll
+    for (int st = 0; st < RPD && st < NSB; ++st) vop[st] = read_v(vl, st);
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase B ----
     if (kMasked) apply_mask(k0);
 #pragma unroll
     for (int st = 0; st < NSB; ++st) {
-      if (st + 1 < NSB) vop[(st + 1) & 1] = read_v(vl, st + 1);
+      if (st + RPD < NSB) vop[(st + RPD) % (RPD + 1)] = read_v(vl, st + RPD);
       const int kk = st / NDB, db = st % NDB;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         const int mi = st * NH + h;
-        oacc[h][db] = Ty::mfma(vop[st & 1], pk[h][kk], oacc[h][db]);
+        oacc[h][db] = Ty::mfma(vop[st % (RPD + 1)], pk[h][kk], oacc[h][db]);
 #pragma unroll
         for (int u = mi * UB / MB; u < (mi + 1) * UB / MB; ++u) b_unit(u);
         __builtin_amdgcn_sched_barrier(0);
@@ -594,12 +594,19 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
   __builtin_amdgcn_s_barrier();
 
+  // Stage indices rotate with the tile index it = kt - kt_begin: K of tile t
+  // sits in stage t % NKST and V in t % NVST.  They are carried as counters
+  // (kst = it % NKST, vprev = (it - 1) % NVST, lks = (it + PF) % NKST,
+  // lvs = (it + PF) % NVST) instead of being recomputed with divisions.
+  int kst = 0, vprev = NVST - 1, lks = PF % NKST, lvs = PF % NVST;
+  auto bump = [](int x, int n) { return x + 1 == n ? 0 : x + 1; };
   auto run_tiles = [&](auto masked_c, int kt_from, int kt_to) __attribute__((always_inline)) {
     for (int kt = kt_from; kt < kt_to; ++kt) {
-      const int it = kt - kt_begin;
-      const int kst = it % NKST, vprev = (it + NVST - 1) % NVST;
-      tile(masked_c, kst, vprev, kt * BC, tile_or_none(kt + PF), (it + PF) % NKST,
-           (it + PF) % NVST);
+      tile(masked_c, kst, vprev, kt * BC, tile_or_none(kt + PF), lks, lvs);
+      kst = bump(kst, NKST);
+      vprev = bump(vprev, NVST);
+      lks = bump(lks, NKST);
+      lvs = bump(lvs, NVST);
       // Tile kt+1 has landed (this wave's share) once at most PF-1 tiles'
       // loads are outstanding; the barrier extends that to the whole
       // work-group.  Every LDS read of this tile was consumed by an MFMA
