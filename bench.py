@@ -4,6 +4,9 @@ One step is one ``fa_fwd`` launch over the whole batch of the workload (all
 of the hot path: tile loads, QK^T, masking, online softmax, PV, epilogue).
 Inputs are generated once, copied to HBM and reused; W untimed steps, then K
 steps timed with events on the launch stream, bracketed by synchronisation.
+The default W is about a second of work: under sustained MFMA load the
+MI355X clock takes on the order of a second to settle, and a few warm-up
+steps alone report it cold (about a quarter slower).
 
 Prints one JSON line: the headline metric (forward TFLOP/s, causal FLOPs
 counted as 4*d per visible pair) plus a ``roofline`` object for the kernel and
@@ -107,8 +110,8 @@ def copy_calibration(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="prefill_8k_d128")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample (0 disables it)")
