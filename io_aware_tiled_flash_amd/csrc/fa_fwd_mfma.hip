@@ -80,6 +80,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float TAU = 8.0f;
 #ifndef FA_RPD
 #define FA_RPD 3
+#endif
+#ifndef FA_UA_PRE
+#define FA_UA_PRE 2
 #endif  // max growth (base 2) tolerated before rescaling
 
 struct TBF16 {
@@ -365,13 +368,18 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // O_h *= alpha_h where some lane's factor differs from 1.  Rare once the
   // running maxima settle (see TAU), so it sits at the end of a tile, where
   // its branch does not split the MFMA/ALU interleaving of the phases.
+  // One test for all halves (a half whose factors are all 1 is multiplied by
+  // 1, which is exact).
   auto rescale = [&]() __attribute__((always_inline)) {
+    bool any_change = alpha[0] != 1.f;
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
-      if (__any(alpha[h] != 1.f)) {
+    for (int h = 1; h < NH; ++h) any_change = any_change || alpha[h] != 1.f;
+    if (__any(any_change)) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[h][db] *= alpha[h];
-      }
+    }
   };
 
   // Elementwise mask of the raw scores (tiles straddling a band edge):
@@ -519,6 +527,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   constexpr int NSB = NPS * NDB, MB = NSB * NH;  // product steps, MFMAs
   constexpr int NDMA = 2 * LOADS_PER_WAVE;       // direct loads per tile
   constexpr int RPD = FA_RPD;                    // operand reads run RPD steps ahead
+  constexpr int UA_PRE = FA_UA_PRE < UA ? FA_UA_PRE : UA;  // units before the first MFMA
   auto tile = [&](auto masked_c, int kst, int vprev, int k0, int lkt, int lks, int lvs)
                   __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked_c)::value;
@@ -530,6 +539,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     u32x4 kop[RPD + 1];
 #pragma unroll
     for (int st = 0; st < RPD && st < NSA; ++st) kop[st] = read_k(kl, st);
+    // The first operand's LDS latency is covered by the first exponentials,
+    // which need no operand; the fence keeps the reads in step order.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < UA_PRE; ++u) a_unit(u);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < NSA; ++st) {
       if (st + RPD < NSA) kop[(st + RPD) % (RPD + 1)] = read_k(kl, st + RPD);
@@ -539,7 +554,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
         const int mi = st * NH + h;
         sacc[h][kb] = Ty::mfma(kop[st % (RPD + 1)], qreg[h][ks], ks == 0 ? f32x16{} : sacc[h][kb]);
 #pragma unroll
-        for (int u = mi * UA / MA; u < (mi + 1) * UA / MA; ++u) a_unit(u);
+        for (int u = UA_PRE + mi * (UA - UA_PRE) / MA; u < UA_PRE + (mi + 1) * (UA - UA_PRE) / MA; ++u)
+          a_unit(u);
         // direct loads of tile t+PF, one after each of the MFMAs 1, 3, 5, ...
         if (mi % 2 == 1 && mi / 2 < NDMA) {
           const int d = mi / 2, i = d >> 1;
@@ -593,6 +609,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // stay in flight.
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
   __builtin_amdgcn_s_barrier();
+  // Kernel arguments arrive through scalar loads, which share the counter
+  // of LDS reads.  Using every argument-derived value the loops or the
+  // epilogue read (buffer descriptors, output pointers) once here settles
+  // the compiler's bookkeeping of those loads before the loops: a scalar load
+  // still pending at a loop entry, or feeding an inline-assembly operand in
+  // a loop, makes it wait for lgkmcnt(0), which also drains the LDS operand
+  // reads that run ahead of the MFMAs.
+  asm volatile("" ::"s"(rk), "s"(rv), "s"(a.o), "s"(a.lse));
 
   // Stage indices rotate with the tile index it = kt - kt_begin: K of tile t
   // sits in stage t % NKST and V in t % NVST.  They are carried as counters
