@@ -209,8 +209,13 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 
   // Tiles are loaded PF tiles ahead of the one being computed.  K needs PF+1
   // stages; V needs PF+2 because the PV products of tile t are issued during
-  // tile t+1.
-  constexpr int NKST = PF + 1, NVST = PF + 2;
+  // tile t+1.  Both get NST = PF+2 stages so that one index, it % NST with
+  // it = kt - kt_begin, names the stages of a tile; the tile loop is unrolled
+  // NST times, which makes every stage offset a compile-time immediate of the
+  // LDS instructions.
+  constexpr int NST = PF + 2;
+  static_assert(NST == 4, "the tile loop below is unrolled four times");
+  constexpr int NKST = NST, NVST = NST;
   constexpr int LOADS_PER_TILE = 2 * LOADS_PER_WAVE;  // per wave, K and V
   static_assert(LOADS_PER_TILE * (PF - 1) < 64, "vmcnt range");
   __shared__ u32x4 k_lds[NKST][TILE_CHUNKS];
@@ -528,9 +533,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   constexpr int NDMA = 2 * LOADS_PER_WAVE;       // direct loads per tile
   constexpr int RPD = FA_RPD;                    // operand reads run RPD steps ahead
   constexpr int UA_PRE = FA_UA_PRE < UA ? FA_UA_PRE : UA;  // units before the first MFMA
-  auto tile = [&](auto masked_c, int kst, int vprev, int k0, int lkt, int lks, int lvs)
-                  __attribute__((always_inline)) {
-    constexpr bool kMasked = decltype(masked_c)::value;
+  // Tile with stage phase P = it % NST: K in stage P, the previous tile's V
+  // in stage P-1, loads of tile it+PF into stage P+PF.
+  auto tile = [&](bool masked, auto phase_c, int k0, int lkt) __attribute__((always_inline)) {
+    constexpr int P = decltype(phase_c)::value;
+    constexpr int kst = P, vprev = (P + NST - 1) % NST, lks = (P + PF) % NST, lvs = lks;
     const char *kl = (const char *)&k_lds[kst][0];
     const char *vl = (const char *)&v_lds[vprev][0];
     const int lk0 = lkt * BC;
@@ -577,7 +584,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     for (int st = 0; st < RPD && st < NSB; ++st) vop[st] = read_v(vl, st);
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase B ----
-    if (kMasked) apply_mask(k0);
+    if (masked) apply_mask(k0);  // per-wave scalar branch at a fence point
 #pragma unroll
     for (int st = 0; st < NSB; ++st) {
       if (st + RPD < NSB) vop[(st + RPD) % (RPD + 1)] = read_v(vl, st + RPD);
@@ -618,53 +625,48 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // reads that run ahead of the MFMAs.
   asm volatile("" ::"s"(rk), "s"(rv), "s"(a.o), "s"(a.lse));
 
-  // Stage indices rotate with the tile index it = kt - kt_begin: K of tile t
-  // sits in stage t % NKST and V in t % NVST.  They are carried as counters
-  // (kst = it % NKST, vprev = (it - 1) % NVST, lks = (it + PF) % NKST,
-  // lvs = (it + PF) % NVST) instead of being recomputed with divisions.
-  int kst = 0, vprev = NVST - 1, lks = PF % NKST, lvs = PF % NVST;
-  auto bump = [](int x, int n) { return x + 1 == n ? 0 : x + 1; };
-  auto run_tiles = [&](auto masked_c, int kt_from, int kt_to) __attribute__((always_inline)) {
-    for (int kt = kt_from; kt < kt_to; ++kt) {
-      tile(masked_c, kst, vprev, kt * BC, tile_or_none(kt + PF), lks, lvs);
-      kst = bump(kst, NKST);
-      vprev = bump(vprev, NVST);
-      lks = bump(lks, NKST);
-      lvs = bump(lvs, NVST);
-      // Tile kt+1 has landed (this wave's share) once at most PF-1 tiles'
-      // loads are outstanding; the barrier extends that to the whole
-      // work-group.  Every LDS read of this tile was consumed by an MFMA
-      // above, so after the barrier the stages read here may be overwritten.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
-      __builtin_amdgcn_s_barrier();
-    }
+  // The work-group's tiles run in groups of NST, each copy of the tile with
+  // its own compile-time stage phase.  The range is padded to a multiple of
+  // NST with tiles past the last visible one: their loads read the
+  // out-of-range index (zero fill) and all their scores are masked, so they
+  // contribute weight 0 and factor 1 (at most NST-1 such tiles per
+  // work-group; none when the visible range is a multiple of 4 tiles, as
+  // for the 256-row work-groups of a causal sequence).
+  //
+  // Every wave runs every tile of the range (the loads and barriers are
+  // shared).  A wave masks a tile elementwise when the tile straddles an edge
+  // of its rows' band or lies outside it; a tile outside the band is simply
+  // fully masked (weights 0, factor 1).
+  const int n_pad = (kt_end - kt_begin + NST - 1) / NST * NST;
+  auto need_mask = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * BC;
+    if (kt >= kt_end) return true;
+    if (MASK == kMaskCausal) return k0 + BC - 1 > wr0;
+    if (MASK == kMaskWindow) return k0 + BC - 1 > wr0 || k0 <= wr1 - a.window;
+    return k0 + BC > S;
   };
-  // Every wave runs every tile of the work-group's range (the loads and
-  // barriers are shared); per wave, the range splits into a masked run at the
-  // window's lower edge, a plain run, and a masked run from the first tile
-  // that reaches past the wave's first row (or the sequence end).  A tile
-  // outside a wave's band is simply fully masked (weights 0, factor 1).
-  // Separate loops rather than a branch between two tile bodies keep the
-  // register allocation of the two copies apart.
-  int plain_begin = kt_begin, plain_end;
-  if (MASK == kMaskNone) {
-    plain_end = S / BC;  // a ragged last tile is masked
-  } else {
-    plain_end = (wr0 + 1) / BC;  // tiles with k0 + BC - 1 <= wr0 need no diagonal mask
-    if (MASK == kMaskWindow && wr1 - a.window >= 0)
-      plain_begin = (wr1 - a.window) / BC + 1;  // tiles with k0 <= wr1 - window are cut
+  // One tile and the end-of-tile synchronisation.  Tile kt+1 has landed
+  // (this wave's share) once at most PF-1 tiles' loads are outstanding; the
+  // barrier extends that to the whole work-group.  Every LDS read of this
+  // tile was consumed by an MFMA above, so after the barrier the stages read
+  // here may be overwritten.
+  auto step = [&](auto phase_c, int kt) __attribute__((always_inline)) {
+    tile(need_mask(kt), phase_c, kt * BC, tile_or_none(kt + PF));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int kt = kt_begin; kt < kt_begin + n_pad; kt += NST) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 2>{}, kt + 2);
+    step(std::integral_constant<int, 3>{}, kt + 3);
   }
-  plain_begin = min(max(plain_begin, kt_begin), kt_end);
-  plain_end = min(max(plain_end, plain_begin), kt_end);
-  if (MASK == kMaskWindow) run_tiles(std::true_type{}, kt_begin, plain_begin);
-  run_tiles(std::false_type{}, plain_begin, plain_end);
-  run_tiles(std::true_type{}, plain_end, kt_end);
   // The last tile: its weights, then its PV products.
   a_start();
 #pragma unroll
   for (int u = 0; u < UA; ++u) a_unit(u);
   a_finish();
-  if (kt_begin < kt_end) o_phase((kt_end - 1 - kt_begin) % NVST);
+  if (n_pad > 0) o_phase(NST - 1);
 
   // Epilogue: one division per row, RNE to the element type, natural-log LSE.
 #pragma unroll
