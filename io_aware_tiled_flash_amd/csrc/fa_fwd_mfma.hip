@@ -293,7 +293,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   f32x16 oacc[NH][NDB];
   f32x16 sacc[NH][NKB];
   u32x4 pk[NH][NPS];  // packed weights of the previous tile, awaiting their PV product
-  float m[NH], l[NH], alpha[NH];
+  float m[NH], m_prev[NH], l[NH];
+  float m_use[NH], lpart[NH];  // offset the exponent arguments use; a tile's weight sum
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
 #pragma unroll
@@ -301,15 +302,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NPS; ++i) pk[h][i] = u32x4{};
     m[h] = -INFINITY;  // running offset, base 2 (equal in lanes q and q^32)
+    m_prev[h] = -INFINITY;  // the offset before the current tile's update
     l[h] = 0.f;        // this lane's share of the running denominator
-    alpha[h] = 1.f;
+    m_use[h] = 0.f;
+    lpart[h] = -0.f;
   }
   // O accumulators and scores stay in VGPRs (the file is built with the
   // VGPR-destination MFMA form): the softmax and the rare rescale then read
   // them directly, without AGPR copies.
-  // The PV products lag one tile: pk / alpha hold the previous tile's
-  // weights and factors until the next tile (or the epilogue) multiplies them
-  // in.  Initially the weights are zero, and so is the V stage they meet.
+  // The PV products lag one tile: pk holds the previous tile's weights until
+  // the next tile (or the epilogue) multiplies them in.  Initially the
+  // weights are zero, and so is the V stage they meet.
 
   // Per-lane LDS byte offsets.  The swizzle XOR is split into a per-lane base
   // and a compile-time part so every operand read is "lane pointer +
@@ -370,20 +373,24 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     }
   };
 
-  // O_h *= alpha_h where some lane's factor differs from 1.  Rare once the
-  // running maxima settle (see TAU), so it sits at the end of a tile, where
-  // its branch does not split the MFMA/ALU interleaving of the phases.
-  // One test for all halves (a half whose factors are all 1 is multiplied by
-  // 1, which is exact).
+  // Rescale where some lane's offset moved.  Rare once the running maxima
+  // settle (see TAU), so it sits at the end of a tile, where its branch does
+  // not split the MFMA/ALU interleaving of the phases.  Both the accumulator and the denominator are rescaled here, by
+  // alpha = exp2(old offset - new offset) (0 from a row with no visible key
+  // so far, whose accumulator is still 0), so the common path computes no
+  // factor at all.  One test covers all halves (a factor of 1 is exact).
   auto rescale = [&]() __attribute__((always_inline)) {
-    bool any_change = alpha[0] != 1.f;
+    bool any_change = m[0] != m_prev[0];
 #pragma unroll
-    for (int h = 1; h < NH; ++h) any_change = any_change || alpha[h] != 1.f;
+    for (int h = 1; h < NH; ++h) any_change = any_change || m[h] != m_prev[h];
     if (__any(any_change)) {
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
+      for (int h = 0; h < NH; ++h) {
+        const float alpha = __builtin_amdgcn_exp2f(m_prev[h] - m_use[h]);
+        l[h] *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[h][db] *= alpha[h];
+        for (int db = 0; db < NDB; ++db) oacc[h][db] *= alpha;
+      }
     }
   };
 
@@ -404,19 +411,10 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   };
 
   // Online softmax, in pieces that the pipeline below places next to MFMA work.
-  // head(h): row maximum of half h's raw scores, new offset and factor.
   // Contraction step kk of the PV product covers, in each lane, the 8 scores
   // sc[kk/2][8*(kk%2) .. +7]; weights are exp2(c*s - offset).
-  // finish(h): l <- l * alpha + (sum of the tile's weights).
-  float m_use[NH], lpart[NH];
-#pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    m_use[h] = 0.f;
-    lpart[h] = -0.f;
-  }
-  auto sm_finish = [&](int h) __attribute__((always_inline)) {
-    l[h] = l[h] * alpha[h] + lpart[h];
-  };
+  // finish(h): l <- l + (sum of the tile's weights).
+  auto sm_finish = [&](int h) __attribute__((always_inline)) { l[h] += lpart[h]; };
 
   // Software pipeline over key tiles (t = current tile):
   //   phase A: S(t) = K_t Q^T on MFMA, next to the exponentials of tile t-1:
@@ -473,22 +471,28 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // Phase B work, in units: 4 * NH partial row maxima (quarter q of half h),
   // NH head finishes (exchange with lane ^ 32, new offset and factor), then
   // 2 * NPS * NH groups of four exponent arguments.
+  // The row maximum is one max3 chain per half: unit q of half h folds the
+  // scores 4q .. 4q+3 of every 32-key block into it.
   constexpr int UB_MAX = 4 * NH, UB_FIN = NH, UB_ARG = 2 * NPS * NH;
   constexpr int UB = UB_MAX + UB_FIN + UB_ARG;
-  float t4b[NH][4];
+  float tb[NH];
   auto b_unit = [&](int u) __attribute__((always_inline)) {
     if (u < UB_MAX) {
       const int h = u / 4, q = u % 4;
-      float t = -INFINITY;
+      float t = q == 0 ? sacc[h][0][0] : tb[h];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        t = fmaxf(t, fmaxf(fmaxf(sacc[h][kb][4 * q], sacc[h][kb][4 * q + 1]),
-                           fmaxf(sacc[h][kb][4 * q + 2], sacc[h][kb][4 * q + 3])));
-      t4b[h][q] = t;
-      pin(t4b[h][q]);
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const int r = 4 * q + i;
+          t = (q == 0 && kb == 0 && i == 0) ? fmaxf(t, sacc[h][kb][r + 1])
+                                            : fmaxf(fmaxf(t, sacc[h][kb][r]), sacc[h][kb][r + 1]);
+        }
+      tb[h] = t;
+      pin(tb[h]);
     } else if (u < UB_MAX + UB_FIN) {
       const int h = u - UB_MAX;
-      float tmax = fmaxf(fmaxf(t4b[h][0], t4b[h][1]), fmaxf(t4b[h][2], t4b[h][3]));
+      float tmax = tb[h];
       const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, tmax),
                                                        __builtin_bit_cast(uint32_t, tmax),
                                                        false, false);
@@ -496,11 +500,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
                    __builtin_bit_cast(float, (uint32_t)sw[1])) * c;  // c > 0 keeps order
       const float m_old = m[h];
       const float m_new = tmax > m_old + TAU ? tmax : m_old;
-      m_use[h] = m_new == -INFINITY ? 0.f : m_new;          // row fully masked so far
-      alpha[h] = __builtin_amdgcn_exp2f(m_old - m_use[h]);  // 1 if unchanged, 0 from -inf
+      // A row with no visible key so far keeps m = -inf; its exponent
+      // arguments use a finite stand-in, so masked scores still give 0.
+      m_use[h] = fmaxf(m_new, -1e30f);
+      m_prev[h] = m_old;
       m[h] = m_new;
       pin(m_use[h]);
-      pin(alpha[h]);
     } else {
       const int v = u - UB_MAX - UB_FIN;
       const int h = v / (2 * NPS), kk = (v / 2) % NPS, part = v % 2;
