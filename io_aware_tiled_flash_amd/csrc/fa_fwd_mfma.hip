@@ -82,8 +82,9 @@ constexpr float TAU = 8.0f;
 #define FA_RPD 3
 #endif
 #ifndef FA_UA_PRE
-#define FA_UA_PRE 2
-#endif  // max growth (base 2) tolerated before rescaling
+#define FA_UA_PRE 6
+#endif
+  // max growth (base 2) tolerated before rescaling
 
 struct TBF16 {
   static constexpr const char *kName = "bf16";
@@ -546,6 +547,22 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     const char *kl = (const char *)&k_lds[kst][0];
     const char *vl = (const char *)&v_lds[vprev][0];
     const int lk0 = lkt * BC;
+    // Direct load d of tile t+PF (K and V alternate), issued after MFMA 2d+1
+    // of phase A (placements over both phases, or all at once, measured no
+    // better).
+    auto dma = [&](int d) __attribute__((always_inline)) {
+      const int i = d >> 1;
+      const int blk = wave * LOADS_PER_WAVE + i;
+      const int pos = 64 * blk + lane;
+      const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
+      const uint32_t off = (uint32_t)((lk0 + r) * D + 8 * cc) * 2u;
+      if (d & 1)
+        load16_to_lds(rv, off, (uint32_t)(uintptr_t)&v_lds[lvs][64 * blk]);
+      else
+        load16_to_lds(rk, off, (uint32_t)(uintptr_t)&k_lds[lks][64 * blk]);
+    };
+    auto dma_slot = [](int d) constexpr { return 2 * d + 1; };
+    static_assert(2 * NDMA <= MA, "direct loads must fit between the score MFMAs");
     // ---- phase A ----
     a_start();
     u32x4 kop[RPD + 1];
@@ -568,18 +585,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
         for (int u = UA_PRE + mi * (UA - UA_PRE) / MA; u < UA_PRE + (mi + 1) * (UA - UA_PRE) / MA; ++u)
           a_unit(u);
-        // direct loads of tile t+PF, one after each of the MFMAs 1, 3, 5, ...
-        if (mi % 2 == 1 && mi / 2 < NDMA) {
-          const int d = mi / 2, i = d >> 1;
-          const int blk = wave * LOADS_PER_WAVE + i;
-          const int pos = 64 * blk + lane;
-          const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
-          const uint32_t off = (uint32_t)((lk0 + r) * D + 8 * cc) * 2u;
-          if (d & 1)
-            load16_to_lds(rv, off, (uint32_t)(uintptr_t)&v_lds[lvs][64 * blk]);
-          else
-            load16_to_lds(rk, off, (uint32_t)(uintptr_t)&k_lds[lks][64 * blk]);
-        }
+#pragma unroll
+        for (int d = 0; d < NDMA; ++d)
+          if (dma_slot(d) == mi) dma(d);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
