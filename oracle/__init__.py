@@ -4,7 +4,7 @@ Only the tests, the package smoke check and the benchmark's CPU-baseline leg
 may import this package; the product path never does.
 """
 from .attention import (attention_probs_ref, attention_ref, attention_rows_ref,
-                        attention_tiled_ref, visible)
+                        attention_tiled_ref, kv_head, visible)
 
 __all__ = ["attention_probs_ref", "attention_ref", "attention_rows_ref",
-           "attention_tiled_ref", "visible"]
+           "attention_tiled_ref", "kv_head", "visible"]

@@ -39,8 +39,15 @@ A row with no visible key (not reachable through the library, whose masks
 always keep the diagonal) gets O = 0 and LSE = -inf; the foundry page's
 "Failure modes" section names such rows as the NaN hazard to guard.
 
-Inputs are any real arrays (numpy or torch CPU) of shape [B, H, S, d]; they are
-converted exactly to fp64 before any arithmetic.
+Grouped key/value heads: the Dev.to article's section "Using it in practice"
+says later variants of the method support grouped-query attention without
+spelling it out.  The plain reading, taken here, is the usual one: K and V
+carry Hkv heads, Hkv divides the H query heads, and query head h attends with
+key/value head h // (H / Hkv) (Hkv = H is ordinary multi-head attention,
+Hkv = 1 multi-query attention).  Nothing else changes.
+
+Inputs are any real arrays (numpy or torch CPU) of shape [B, H, S, d] (K and V:
+[B, Hkv, S, d]); they are converted exactly to fp64 before any arithmetic.
 """
 from __future__ import annotations
 
@@ -49,7 +56,7 @@ import math
 import numpy as np
 
 __all__ = ["visible", "attention_ref", "attention_probs_ref", "attention_tiled_ref",
-           "attention_rows_ref"]
+           "attention_rows_ref", "kv_head"]
 
 _MASKS = ("none", "causal", "window")
 
@@ -130,31 +137,41 @@ def attention_rows_ref(q, k, v, rows, mask="none", window=None, scale=None):
     return o, lse
 
 
+def kv_head(h: int, n_heads: int, n_kv_heads: int) -> int:
+    """Key/value head that query head h attends with (grouped heads)."""
+    if n_kv_heads < 1 or n_heads % n_kv_heads:
+        raise ValueError(f"{n_kv_heads} key/value heads do not divide {n_heads} query heads")
+    return h // (n_heads // n_kv_heads)
+
+
 def attention_ref(q, k, v, mask="none", window=None, scale=None, row_chunk=2048,
                   heads=None):
-    """Exact fp64 attention over [B, H, S, d] inputs.
+    """Exact fp64 attention over [B, H, S, d] queries and [B, Hkv, S, d] keys
+    and values (Hkv divides H; Hkv = H is plain multi-head attention).
 
     For every (b, h) and every chunk of at most ``row_chunk`` query rows the
-    scaled score block and its probabilities are materialised in full.
-    ``heads`` optionally restricts the work to a list of (b, h) pairs (the
-    other heads of the result are left as NaN).  Returns (O [B,H,S,d],
-    LSE [B,H,S]) in fp64.
+    scaled score block and its probabilities are materialised in full, against
+    key/value head kv_head(h, H, Hkv).  ``heads`` optionally restricts the work
+    to a list of (b, h) pairs (the other heads of the result are left as NaN).
+    Returns (O [B,H,S,d], LSE [B,H,S]) in fp64.
     """
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
     B, H, S, d = q.shape
-    if k.shape != (B, H, S, d) or v.shape[:3] != (B, H, S):
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, d) or v.shape[:3] != (B, Hkv, S):
         raise ValueError("q, k, v shapes disagree")
     dv = v.shape[-1]
     o = np.full((B, H, S, dv), np.nan)
     lse = np.full((B, H, S), np.nan)
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
+        g = kv_head(h, H, Hkv)
         for r0 in range(0, S, row_chunk):
             rows = np.arange(r0, min(S, r0 + row_chunk))
             o[b, h, rows], lse[b, h, rows] = attention_rows_ref(
-                q[b, h], k[b, h], v[b, h], rows, mask, window, scale)
+                q[b, h], k[b, g], v[b, g], rows, mask, window, scale)
     return o, lse
 
 

@@ -19,7 +19,7 @@ import scipy.special
 import torch
 
 from oracle import (attention_probs_ref, attention_ref, attention_rows_ref,
-                    attention_tiled_ref, visible)
+                    attention_tiled_ref, kv_head, visible)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -335,6 +335,76 @@ def test_brute_force_mpmath(mask, window):
     o_mp, lse_mp = _mp_attention(q, k, v, scale, visible_torchless(S, mask, window))
     np.testing.assert_allclose(o, o_mp, atol=1e-13, rtol=0)
     np.testing.assert_allclose(lse, lse_mp, atol=1e-13, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# grouped key/value heads (query head h uses key/value head h // (H / Hkv))
+# --------------------------------------------------------------------------
+
+def _sdpa_gqa(q, k, v, mask, window, scale):
+    """torch's own grouped-query attention (enable_gqa) in fp64, plus the
+    logsumexp of the visible scaled scores through scipy."""
+    S = q.shape[2]
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    if mask == "causal":
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                            scale=scale, enable_gqa=True)
+    else:
+        vis = torch.from_numpy(visible_torchless(S, mask, window))
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=vis,
+                                                            scale=scale, enable_gqa=True)
+    group = q.shape[1] // k.shape[1]
+    kr = torch.repeat_interleave(tk, group, dim=1)
+    scores = torch.matmul(tq, kr.transpose(-1, -2).contiguous()).numpy() * scale
+    scores = np.where(visible_torchless(S, mask, window), scores, -np.inf)
+    return o.numpy(), scipy.special.logsumexp(scores, axis=-1)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 3), (4, 1), (8, 4), (3, 3)])
+@pytest.mark.parametrize("mask,window", [("none", None), ("causal", None), ("window", 5)])
+def test_grouped_heads_against_torch_sdpa_fp64(H, Hkv, mask, window):
+    B, S, d = 2, 19, 8
+    scale = 1.0 / math.sqrt(d)
+    q = _rand((B, H, S, d), 60)
+    k, v = _rand((B, Hkv, S, d), 61), _rand((B, Hkv, S, d), 62)
+    o, lse = attention_ref(q, k, v, mask, window, scale=scale)
+    want_o, want_lse = _sdpa_gqa(q, k, v, mask, window, scale)
+    np.testing.assert_allclose(o, want_o, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, want_lse, atol=1e-12, rtol=0)
+
+
+def test_grouped_heads_share_their_key_value_head():
+    # Query heads of one group that carry the same queries give the same rows;
+    # heads of different groups differ.
+    B, H, Hkv, S, d = 1, 6, 2, 11, 4
+    q1 = _rand((1, 1, S, d), 63)
+    q = np.repeat(q1, H, axis=1)
+    k, v = _rand((B, Hkv, S, d), 64), _rand((B, Hkv, S, d), 65)
+    o, lse = attention_ref(q, k, v, "causal")
+    for h in range(H):
+        assert kv_head(h, H, Hkv) == h // 3
+        np.testing.assert_array_equal(o[0, h], o[0, 3 * (h // 3)])
+    assert not np.allclose(o[0, 0], o[0, 3])
+
+
+def test_grouped_heads_reject_non_dividing_counts():
+    q, k = _rand((1, 4, 5, 2), 66), _rand((1, 3, 5, 2), 67)
+    with pytest.raises(ValueError):
+        attention_ref(q, k, k)
+    with pytest.raises(ValueError):
+        kv_head(0, 4, 0)
+
+
+def test_grouped_heads_reject_wrong_head_mapping():
+    # A plausible mistake (interleaved instead of contiguous groups) is caught
+    # by the torch pin.
+    B, H, Hkv, S, d = 1, 4, 2, 7, 4
+    q = _rand((B, H, S, d), 68)
+    k, v = _rand((B, Hkv, S, d), 69), _rand((B, Hkv, S, d), 70)
+    want_o, _ = _sdpa_gqa(q, k, v, "none", None, 0.5)
+    wrong = np.stack([attention_rows_ref(q[0, h], k[0, h % Hkv], v[0, h % Hkv], np.arange(S),
+                                         "none", None, 0.5)[0] for h in range(H)])[None]
+    assert not np.allclose(wrong, want_o, atol=1e-6)
 
 
 # --------------------------------------------------------------------------
