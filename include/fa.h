@@ -95,6 +95,27 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
                  int64_t window, float scale, void *stream);
 
 /*
+ * fa_fwd_gqa -- fa_fwd with grouped key/value heads (grouped-query attention;
+ * multi-query attention when Hkv == 1).  The Dev.to article on FlashAttention,
+ * section "Using it in practice", names grouped-query attention among the
+ * patterns later variants of the method support; the computation per query
+ * head is exactly fa_fwd's, against one shared key/value head.
+ *
+ * q, o    : [B, H, S, d] as in fa_fwd.
+ * k, v    : [B, Hkv, S, d] contiguous, `dtype`.  Query head h of batch b
+ *           attends with key/value head h / (H / Hkv) of batch b (contiguous
+ *           groups of H / Hkv query heads share one key/value head).
+ * lse     : [B, H, S] fp32, as in fa_fwd.
+ * Hkv     : >= 1 and dividing H.  Hkv == H gives exactly fa_fwd.
+ * Every other argument, the ownership rules and the error list are those of
+ * fa_fwd; in addition FA_EINVAL is returned when Hkv < 1 or Hkv does not
+ * divide H, and the overlap checks use the [B, Hkv, S, d] extent of k and v.
+ */
+fa_status fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t d, int dtype,
+                     int mask, int64_t window, float scale, void *stream);
+
+/*
  * fa_query -- name the kernel instance fa_fwd would launch for (d, dtype,
  * mask), without launching anything or touching the GPU.  Writes a
  * NUL-terminated name into kernel_name[0..len) (truncated if needed; may be

@@ -1,8 +1,8 @@
 """MI355X (gfx950) exact-attention forward: Python binding of ``libfa.so``.
 
-The functions ``fa_fwd``, ``fa_query``, ``fa_status_str``, ``fa_last_error`` and
-``fa_abi_version`` mirror the C ABI declared in ``include/fa.h`` one to one
-(argument marshalling only).  ``forward`` is the tensor-level convenience
+The functions ``fa_fwd``, ``fa_fwd_gqa``, ``fa_query``, ``fa_status_str``,
+``fa_last_error`` and ``fa_abi_version`` mirror the C ABI declared in
+``include/fa.h`` one to one (argument marshalling only).  ``forward`` is the tensor-level convenience
 wrapper: it checks the tensors, allocates ``o`` and ``lse`` with torch and
 launches on torch's current stream.  Every arithmetic step runs in the HIP
 kernels; there is no Python or CPU fallback, and a missing library is an
@@ -14,7 +14,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_query", "fa_status_str", "fa_last_error",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_gqa", "fa_query", "fa_status_str", "fa_last_error",
            "fa_abi_version", "forward", "library_path", "DTYPES", "MASKS",
            "FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
 
@@ -51,6 +51,10 @@ def _load():
     lib.fa_fwd.restype = c_int
     lib.fa_fwd.argtypes = [ctypes.c_void_p] * 5 + [i64] * 4 + [c_int, c_int, i64,
                                                                ctypes.c_float, ctypes.c_void_p]
+    lib.fa_fwd_gqa.restype = c_int
+    lib.fa_fwd_gqa.argtypes = [ctypes.c_void_p] * 5 + [i64] * 5 + [c_int, c_int, i64,
+                                                                   ctypes.c_float,
+                                                                   ctypes.c_void_p]
     lib.fa_query.restype = c_int
     lib.fa_query.argtypes = [i64, c_int, c_int, ctypes.c_char_p, ctypes.c_size_t]
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -79,6 +83,14 @@ def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, d: 
     """Raw launch on device pointers; returns the fa_status code."""
     return _load().fa_fwd(q, k, v, o, lse, B, H, S, d, dtype, mask, window,
                           ctypes.c_float(scale), stream)
+
+
+def fa_fwd_gqa(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Hkv: int, S: int,
+               d: int, dtype: int, mask: int, window: int, scale: float,
+               stream: int | None) -> int:
+    """Raw launch with Hkv key/value heads; returns the fa_status code."""
+    return _load().fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, S, d, dtype, mask, window,
+                              ctypes.c_float(scale), stream)
 
 
 def fa_query(d: int, dtype: int, mask: int) -> str:
@@ -116,6 +128,8 @@ def forward(q, k, v, mask: str = "none", window: int | None = None,
             scale: float | None = None, out=None, lse=None, stream=None):
     """Exact attention forward on [B, H, S, d] device tensors.
 
+    k and v may carry fewer heads than q (grouped-query attention: [B, Hkv, S,
+    d] with Hkv dividing H; query head h uses key/value head h // (H // Hkv)).
     Returns (o, lse): o has q's shape and dtype, lse is fp32 [B, H, S] (natural
     log).  ``scale`` defaults to 1/sqrt(d).  Launches on ``stream`` (a torch
     stream) or torch's current stream; asynchronous like any torch op.
@@ -128,8 +142,10 @@ def forward(q, k, v, mask: str = "none", window: int | None = None,
             raise FaError(FA_EINVAL, f"{name} must be a device tensor")
         if t.dim() != 4 or not t.is_contiguous():
             raise FaError(FA_EINVAL, f"{name} must be a contiguous [B, H, S, d] tensor")
-    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
-        raise FaError(FA_EINVAL, "q, k, v must share shape and dtype")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2:] != k.shape[2:]:
+        raise FaError(FA_EINVAL, "k and v must be [B, Hkv, S, d] with q's B, S and d")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FaError(FA_EINVAL, "q, k, v must share a dtype")
     if not (q.device == k.device == v.device):
         raise FaError(FA_EINVAL, "q, k, v must be on one device")
     B, H, S, d = q.shape
@@ -146,10 +162,16 @@ def forward(q, k, v, mask: str = "none", window: int | None = None,
         raise FaError(FA_EINVAL, "lse must be a contiguous fp32 [B, H, S] tensor")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    Hkv = k.shape[1]
     with torch.cuda.device(q.device):
-        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                    B, H, S, d, dt, MASKS[mask], int(window or 0), float(scale),
-                    stream.cuda_stream)
+        if Hkv == H:
+            st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr(), B, H, S, d, dt, MASKS[mask], int(window or 0),
+                        float(scale), stream.cuda_stream)
+        else:
+            st = fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, H, Hkv, S, d, dt, MASKS[mask],
+                            int(window or 0), float(scale), stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, fa_last_error())
     return out, lse

@@ -55,22 +55,23 @@ const char *dtype_name(int dt) {
   return dt == FA_F32 ? "f32" : dt == FA_F16 ? "f16" : dt == FA_BF16 ? "bf16" : "?";
 }
 
-}  // namespace
-
-extern "C" {
-
-fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
-                 int64_t H, int64_t S, int64_t d, int dtype, int mask, int64_t window,
-                 float scale, void *stream) {
+// The forward pass for H query heads over Hkv key/value heads (Hkv == H is
+// plain multi-head attention).  `name` labels log lines.
+fa_status fwd_impl(const char *name, const void *q, const void *k, const void *v, void *o,
+                   float *lse, int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t d,
+                   int dtype, int mask, int64_t window, float scale, void *stream) {
   g_err[0] = '\0';
   if (!q || !k || !v || !o || !lse) return fail(FA_EINVAL, "null pointer argument");
   const void *ptrs[5] = {q, k, v, o, lse};
   for (int i = 0; i < 5; ++i)
     if ((uintptr_t)ptrs[i] % 16 != 0)
       return fail(FA_EINVAL, "pointer argument %d is not 16-byte aligned", i);
-  if (B < 1 || H < 1 || S < 1 || d < 1)
-    return fail(FA_EINVAL, "sizes must be >= 1 (B=%lld H=%lld S=%lld d=%lld)", (long long)B,
-                (long long)H, (long long)S, (long long)d);
+  if (B < 1 || H < 1 || Hkv < 1 || S < 1 || d < 1)
+    return fail(FA_EINVAL, "sizes must be >= 1 (B=%lld H=%lld Hkv=%lld S=%lld d=%lld)",
+                (long long)B, (long long)H, (long long)Hkv, (long long)S, (long long)d);
+  if (H % Hkv != 0)
+    return fail(FA_EINVAL, "key/value heads (%lld) must divide query heads (%lld)",
+                (long long)Hkv, (long long)H);
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
     return fail(FA_EINVAL, "unknown dtype %d", dtype);
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_WINDOW)
@@ -81,21 +82,22 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
   if (!isfinite(scale)) return fail(FA_EINVAL, "scale must be finite");
 
   const int64_t esz = dtype == FA_F32 ? 4 : 2;
-  int64_t bh, rows, elems, bytes, row_bytes, head_bytes, lse_bytes;
+  int64_t bh, rows, elems, bytes, row_bytes, head_bytes, lse_bytes, bhkv, kv_bytes;
   if (!mul_ok(B, H, &bh) || !mul_ok(bh, S, &rows) || !mul_ok(rows, d, &elems) ||
       !mul_ok(elems, esz, &bytes) || !mul_ok(rows, 4, &lse_bytes) ||
-      !mul_ok(d, esz, &row_bytes) || !mul_ok(S, row_bytes, &head_bytes))
+      !mul_ok(d, esz, &row_bytes) || !mul_ok(S, row_bytes, &head_bytes) ||
+      !mul_ok(B, Hkv, &bhkv) || !mul_ok(bhkv, head_bytes, &kv_bytes))
     return fail(FA_EINVAL, "tensor size overflows 64-bit byte counts");
   if (head_bytes > (int64_t)INT32_MAX)
     return fail(FA_EINVAL, "one head's [S, d] slab (%lld bytes) exceeds 2 GiB",
                 (long long)head_bytes);
   if (bh > (int64_t)INT32_MAX || rows > (int64_t)INT64_MAX / 2)
     return fail(FA_EINVAL, "batch*heads too large");
-  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) ||
-      overlaps(o, bytes, v, bytes) || overlaps(o, bytes, lse, lse_bytes))
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, kv_bytes) ||
+      overlaps(o, bytes, v, kv_bytes) || overlaps(o, bytes, lse, lse_bytes))
     return fail(FA_EINVAL, "output o overlaps an input or lse");
-  if (overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
-      overlaps(lse, lse_bytes, v, bytes))
+  if (overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
+      overlaps(lse, lse_bytes, v, kv_bytes))
     return fail(FA_EINVAL, "lse overlaps an input");
 
   // A window that covers the whole sequence is the causal mask.
@@ -110,6 +112,7 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
   a.lse = lse;
   a.B = (int)B;
   a.H = (int)H;
+  a.Hkv = (int)Hkv;
   a.S = (int)S;
   a.window = eff_mask == FA_MASK_WINDOW ? (int)window : 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -123,14 +126,32 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
   if (nq * bh > (int64_t)INT32_MAX) return fail(FA_EINVAL, "grid too large");
 
   if (log_enabled())
-    fprintf(stderr, "fa_fwd: kernel=%s grid=%lld block=%d B=%lld H=%lld S=%lld d=%lld\n",
-            info.name, (long long)(nq * bh), info.threads, (long long)B, (long long)H,
-            (long long)S, (long long)d);
+    fprintf(stderr, "%s: kernel=%s grid=%lld block=%d B=%lld H=%lld Hkv=%lld S=%lld d=%lld\n",
+            name, info.name, (long long)(nq * bh), info.threads, (long long)B, (long long)H,
+            (long long)Hkv, (long long)S, (long long)d);
 
   dispatch(dtype, (int)d, eff_mask, &a, (hipStream_t)stream, true, &info, &err);
   if (err != hipSuccess)
     return fail(FA_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                 int64_t H, int64_t S, int64_t d, int dtype, int mask, int64_t window,
+                 float scale, void *stream) {
+  return fwd_impl("fa_fwd", q, k, v, o, lse, B, H, H, S, d, dtype, mask, window, scale,
+                  stream);
+}
+
+fa_status fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t d, int dtype,
+                     int mask, int64_t window, float scale, void *stream) {
+  return fwd_impl("fa_fwd_gqa", q, k, v, o, lse, B, H, Hkv, S, d, dtype, mask, window, scale,
+                  stream);
 }
 
 fa_status fa_query(int64_t d, int dtype, int mask, char *kernel_name, size_t len) {

@@ -32,15 +32,17 @@ __global__ __launch_bounds__(64, 1) void fa_fwd_f32_kernel(FwdArgs a) {
   const int S = a.S;
   const int BH = a.B * a.H;
   const int nq = (S + BR - 1) / BR;
-  const int bh = blockIdx.x % BH;
+  const HeadPair hp = head_of_slot(blockIdx.x % BH, a.B, a.H, a.Hkv);
+  const int bh = hp.q;
   int qt = blockIdx.x / BH;
   if (MASK != kMaskNone) qt = nq - 1 - qt;
   const int q0 = qt * BR;
   const int row = q0 + tid;
-  const size_t head_off = (size_t)bh * (size_t)S * D;
+  const size_t head_off = (size_t)bh * (size_t)S * D;   // q, o
+  const size_t kv_off = (size_t)hp.kv * (size_t)S * D;  // k, v
   const float4 *qh = (const float4 *)((const float *)a.q + head_off);
-  const float4 *kh = (const float4 *)((const float *)a.k + head_off);
-  const float4 *vh = (const float4 *)((const float *)a.v + head_off);
+  const float4 *kh = (const float4 *)((const float *)a.k + kv_off);
+  const float4 *vh = (const float4 *)((const float *)a.v + kv_off);
 
   float q[D], o[D];
 #pragma unroll

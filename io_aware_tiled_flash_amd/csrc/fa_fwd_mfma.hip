@@ -231,16 +231,18 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   const int BH = a.B * a.H;
   const int nq = (S + BR - 1) / BR;
 
-  const int bh = blockIdx.x % BH;
+  const HeadPair hp = head_of_slot(blockIdx.x % BH, a.B, a.H, a.Hkv);
+  const int bh = hp.q;
   int qt = blockIdx.x / BH;
   if (MASK != kMaskNone) qt = nq - 1 - qt;  // heaviest query tiles first
   const int q0 = qt * BR;
 
-  const size_t head_off = (size_t)bh * (size_t)S * D;  // elements
+  const size_t head_off = (size_t)bh * (size_t)S * D;     // q, o (elements)
+  const size_t kv_off = (size_t)hp.kv * (size_t)S * D;    // k, v (elements)
   const uint32_t head_bytes = (uint32_t)S * D * 2u;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t *)a.q + head_off, head_bytes);
-  const u32x4 rk = rsrc_words((const uint16_t *)a.k + head_off, head_bytes);
-  const u32x4 rv = rsrc_words((const uint16_t *)a.v + head_off, head_bytes);
+  const u32x4 rk = rsrc_words((const uint16_t *)a.k + kv_off, head_bytes);
+  const u32x4 rv = rsrc_words((const uint16_t *)a.v + kv_off, head_bytes);
 
   // The softmax runs on c * s with c > 0: a negative scale is applied by
   // flipping the sign bits of Q (exact in bf16 and fp16), and a zero scale

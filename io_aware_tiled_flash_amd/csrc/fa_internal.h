@@ -12,13 +12,32 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // Arguments of one forward launch, already validated on the host.
 struct FwdArgs {
-  const void *q, *k, *v;   // [B, H, S, d] contiguous
+  const void *q;           // [B, H, S, d] contiguous
+  const void *k, *v;       // [B, Hkv, S, d] contiguous; Hkv divides H
   void *o;                 // [B, H, S, d] contiguous
   float *lse;              // [B, H, S]
-  int B, H, S;
+  int B, H, Hkv, S;
   int window;              // used by the sliding-window instances only
   float scale_log2;        // scale * log2(e): scores are kept in base-2 units
 };
+
+// Query head (index into the B*H heads of q, o, lse) and key/value head
+// (index into the B*Hkv heads of k, v) served by work-group slot s in
+// [0, B*H).  Query head h of batch b reads key/value head h / (H / Hkv).
+// Slots run over every key/value head first and then over the members of
+// each group, so when B*Hkv is a multiple of 8 the query heads of one group
+// land on the same XCD (work-groups are dealt round-robin over the 8 XCDs)
+// and share its L2 for their K/V tiles.  With Hkv == H the mapping is the
+// identity.
+struct HeadPair {
+  int q, kv;
+};
+__device__ inline HeadPair head_of_slot(int s, int B, int H, int Hkv) {
+  const int group = H / Hkv, n_kv = B * Hkv;
+  const int j = s / n_kv, kvi = s - j * n_kv;
+  const int b = kvi / Hkv, hk = kvi - b * Hkv;
+  return HeadPair{b * H + hk * group + j, kvi};
+}
 
 // What a launch would look like, for logging and fa_query.
 struct LaunchInfo {

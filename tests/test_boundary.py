@@ -29,7 +29,8 @@ def _declared_functions():
 
 def test_library_builds_and_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == ["fa_abi_version", "fa_fwd", "fa_last_error", "fa_query", "fa_status_str"]
+    assert names == ["fa_abi_version", "fa_fwd", "fa_fwd_gqa", "fa_last_error", "fa_query",
+                     "fa_status_str"]
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -105,6 +106,39 @@ def test_invalid_arguments_are_rejected_before_any_launch(kw, needle):
 def test_unsupported_configuration_is_an_error_not_a_fallback(kw):
     assert _call(**kw) == fa.FA_EUNSUPPORTED
     assert "no kernel" in fa.fa_last_error()
+
+
+def _call_gqa(**kw):
+    args = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
+                B=1, H=8, Hkv=2, S=128, d=128, dtype=2, mask=1, window=0, scale=0.088,
+                stream=None)
+    args.update(kw)
+    return fa.fa_fwd_gqa(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                         args["H"], args["Hkv"], args["S"], args["d"], args["dtype"],
+                         args["mask"], args["window"], args["scale"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(Hkv=0), "sizes"), (dict(Hkv=-2), "sizes"), (dict(Hkv=3), "divide"),
+    (dict(H=6, Hkv=4), "divide"), (dict(H=2, Hkv=8), "divide"),
+    (dict(q=0), "null"), (dict(v=A + 128 * MB + 8), "aligned"), (dict(mask=4), "mask"),
+    # o ([1,8,128,128] bf16 = 256 KiB) placed inside v's [1,2,128,128] extent (64 KiB)
+    (dict(o=A + 128 * MB + 32 * 1024), "overlap"),
+    (dict(lse=A + 64 * MB + 1024), "overlap"),
+])
+def test_grouped_heads_invalid_arguments(kw, needle):
+    st = _call_gqa(**kw)
+    assert st == fa.FA_EINVAL, (st, fa.fa_last_error())
+    assert needle in fa.fa_last_error()
+
+
+def test_grouped_heads_overlap_uses_the_key_value_extent():
+    # k/v hold Hkv = 2 heads (64 KiB each); an o placed right after v's real
+    # extent (but inside where 8 heads would reach) is not an overlap, so the
+    # call proceeds to dispatch (an unsupported d keeps anything from launching).
+    assert _call_gqa(o=A + 128 * MB + 64 * 1024, d=96) == fa.FA_EUNSUPPORTED
+    assert _call_gqa(H=8, Hkv=8, d=96) == fa.FA_EUNSUPPORTED
+    assert _call_gqa(H=8, Hkv=1, d=96) == fa.FA_EUNSUPPORTED
 
 
 def test_window_argument_ignored_without_window_mask():

@@ -63,11 +63,13 @@ def _sample_rows(S, n, rng):
 def _check_sampled(q, k, v, o, lse, mask, window, scale, dtype, label, n_rows=48, seed=0):
     rng = np.random.default_rng(seed)
     B, H, S, d = q.shape
+    group = H // k.shape[1]  # query heads per key/value head
     worst_o = worst_l = 0.0
     for b in range(B):
         for h in range(H):
             rows = _sample_rows(S, n_rows, rng)
-            o_ref, lse_ref = attention_rows_ref(q[b, h], k[b, h], v[b, h], rows, mask, window,
+            g = h // group
+            o_ref, lse_ref = attention_rows_ref(q[b, h], k[b, g], v[b, g], rows, mask, window,
                                                 scale)
             worst_o = max(worst_o, np.abs(o[b, h, rows].double().numpy() - o_ref).max())
             worst_l = max(worst_l, np.abs(lse[b, h, rows].double().numpy() - lse_ref).max())
@@ -108,24 +110,28 @@ def test_worked_example_padded(dtype):
 @pytest.mark.parametrize("name", ["tiny_f32", "causal_d64", "causal_d64_outliers"])
 def test_small_workloads_full(name):
     w = WORKLOADS[name]
-    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
+    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers, w.kv_heads)
     _check_full(q, k, v, w.mask, w.window or None, w.scale, w.dtype, name)
 
 
-@pytest.mark.parametrize("name", ["prefill_8k_d128", "window_18k_d128", "full_d256_f16"])
+@pytest.mark.parametrize("name", ["prefill_8k_d128", "window_18k_d128", "full_d256_f16",
+                                  "prefill_8k_d128_gqa4"])
 def test_large_workloads_sampled(name):
     w = WORKLOADS[name]
     _say(f"{name}: generating inputs")
-    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
+    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers, w.kv_heads)
     _say(f"{name}: launching")
     o, lse = _run(q, k, v, w.mask, w.window or None, w.scale)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     # |O| is a convex combination of V rows, so it never exceeds max |V|
     assert float(o.float().abs().max()) <= float(v.float().abs().max()) * (1 + 1e-2)
-    if w.mask != "none":  # causal/window row 0 sees only key 0
-        s00 = (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1) * w.scale
+    if w.mask != "none":  # causal/window row 0 sees only key 0 (of its key/value head)
+        group = w.H // w.kv_heads
+        k0 = torch.repeat_interleave(k[:, :, 0], group, dim=1)
+        v0 = torch.repeat_interleave(v[:, :, 0], group, dim=1)
+        s00 = (q[:, :, 0].double() * k0.double()).sum(-1) * w.scale
         assert float((lse[:, :, 0].double() - s00).abs().max()) <= LSE_TOL
-        assert float((o[:, :, 0].float() - v[:, :, 0].float()).abs().max()) == 0.0
+        assert float((o[:, :, 0].float() - v0.float()).abs().max()) == 0.0
     _say(f"{name}: oracle rows")
     _check_sampled(q, k, v, o, lse, w.mask, w.window or None, w.scale, w.dtype, name)
 
@@ -217,7 +223,7 @@ def test_window_one_less_than_sequence():
 
 def test_deterministic_repeat():
     w = WORKLOADS["causal_d64_outliers"]
-    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
+    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers, w.kv_heads)
     _say("determinism")
     runs = [_run(q, k, v, "causal", None, w.scale) for _ in range(3)]
     for o, lse in runs[1:]:
@@ -237,3 +243,37 @@ def test_outputs_do_not_touch_neighbours():
     torch.cuda.synchronize()
     assert bool((big[:q.numel()] == 7.0).all()) and bool((big[2 * q.numel():] == 7.0).all())
     assert bool((lbig[:260] == 9.0).all()) and bool((lbig[520:] == 9.0).all())
+
+
+# --------------------------------------------------------------------------
+# grouped key/value heads (fa_fwd_gqa): query head h uses key/value head
+# h // (H / Hkv)
+# --------------------------------------------------------------------------
+
+GQA_CASES = [("bf16", 128, "causal", 8, 2, 300), ("bf16", 64, "none", 6, 3, 257),
+             ("f16", 128, "window", 4, 1, 333), ("f16", 256, "causal", 4, 2, 130),
+             ("bf16", 128, "none", 16, 8, 65), ("f32", 64, "causal", 4, 2, 100),
+             ("f32", 128, "none", 3, 1, 77)]
+
+
+@pytest.mark.parametrize("dtype,d,mask,H,Hkv,S", GQA_CASES)
+def test_grouped_heads_full(dtype, d, mask, H, Hkv, S):
+    window = 37 if mask == "window" else None
+    q, k, v = make_inputs(2, H, S, d, dtype, seed=H * 100 + Hkv * 10 + d, Hkv=Hkv)
+    _check_full(q, k, v, mask, window, 1.0 / math.sqrt(d), dtype,
+                f"gqa {dtype} d={d} {mask} H={H} Hkv={Hkv} S={S}")
+
+
+def test_grouped_heads_equal_repeated_heads_bitwise():
+    # Grouping is exactly plain attention on repeated key/value heads: the
+    # kernel must produce the same bits either way.
+    q, k, v = make_inputs(1, 8, 200, 128, "bf16", seed=21, Hkv=2)
+    dev = torch.device("cuda:0")
+    _say("gqa vs repeated heads, bitwise")
+    og, lg = fa.forward(q.to(dev), k.to(dev), v.to(dev), mask="causal")
+    kr = torch.repeat_interleave(k, 4, dim=1).contiguous()
+    vr = torch.repeat_interleave(v, 4, dim=1).contiguous()
+    om, lm = fa.forward(q.to(dev), kr.to(dev), vr.to(dev), mask="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(og.cpu(), om.cpu())
+    assert torch.equal(lg.cpu(), lm.cpu())

@@ -50,3 +50,23 @@ def test_headline_work_figures():
     assert abs(WORKLOADS["full_d256_f16"].flops() - 1.100e12) / 1.1e12 < 1e-3
     assert abs(WORKLOADS["causal_d64"].flops() - 2.150e9) / 2.15e9 < 1e-3
     assert WORKLOADS["tiny_f32"].flops() == 4 * 64 * 2 * 256 * 256
+
+
+def test_grouped_heads_generator_shapes_and_mha_identity():
+    q, k, v = make_inputs(2, 8, 40, 16, "bf16", seed=9, Hkv=2)
+    assert q.shape == (2, 8, 40, 16) and k.shape == v.shape == (2, 2, 40, 16)
+    # Hkv == H draws exactly the plain multi-head inputs
+    a = make_inputs(1, 4, 33, 8, "f16", seed=4)
+    b = make_inputs(1, 4, 33, 8, "f16", seed=4, Hkv=4)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_grouped_workload_counts():
+    w = WORKLOADS["prefill_8k_d128_gqa4"]
+    m = WORKLOADS["prefill_8k_d128"]
+    assert w.kv_heads == 8 and m.kv_heads == 32
+    assert w.flops() == m.flops()
+    # Q and O are the same; K and V shrink by the group size (4)
+    esz = 2
+    assert m.compulsory_bytes() - w.compulsory_bytes() == 2 * (32 - 8) * 8192 * 128 * esz

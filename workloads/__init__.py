@@ -7,18 +7,21 @@ independent of each other.
 
 Recipe (applies to every workload):
   * generator: ``numpy.random.Generator(PCG64(seed))``;
-  * draw order: Q, then K, then V, each ``standard_normal([B, H, S, d],
-    dtype=float32)`` in C order, multiplied by ``sigma``;
+  * draw order: Q, then K, then V, each ``standard_normal(shape,
+    dtype=float32)`` in C order, multiplied by ``sigma``; the shape is
+    [B, H, S, d] for Q and [B, Hkv, S, d] for K and V (Hkv = H unless the
+    workload has grouped key/value heads);
   * rounding: round-to-nearest-even to the storage dtype (torch CPU ``.to``);
-  * optional outliers: after the three draws, for every (b, h) in (b, h)
+  * optional outliers: after the three draws, for every (b, h) of K in (b, h)
     order, ``rng.choice(S, floor(0.01 * S), replace=False)`` picks key rows that
     are multiplied by 8 (a power of two, so scaling before or after rounding
     gives identical bits).
 
 The named workloads are the five attention configurations the benchmark and
 the parity tests use (tiny fp32, causal d=64, long causal prefill d=128,
-sliding-window d=128, non-causal d=256 fp16) plus the outlier variant of the
-causal d=64 case.
+sliding-window d=128, non-causal d=256 fp16), the outlier variant of the
+causal d=64 case, and the long causal prefill with grouped key/value heads
+(32 query heads over 8 key/value heads).
 """
 from __future__ import annotations
 
@@ -48,6 +51,11 @@ class Workload:
     sigma: float = 1.0
     seed: int = 0
     outliers: bool = False
+    Hkv: int = 0         # key/value heads; 0 means H (plain multi-head attention)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -77,7 +85,8 @@ class Workload:
         """Q, K, V read once plus O and the fp32 LSE written once."""
         esz = {"f32": 4, "f16": 2, "bf16": 2}[self.dtype]
         n = self.B * self.H * self.S
-        return 4 * n * self.d * esz + 4 * n
+        nkv = self.B * self.kv_heads * self.S
+        return (2 * n + 2 * nkv) * self.d * esz + 4 * n
 
 
 WORKLOADS = {
@@ -91,16 +100,19 @@ WORKLOADS = {
                                 window=4096, seed=1003),
     "full_d256_f16": Workload("full_d256_f16", 4, 16, 4096, 256, "f16", "none",
                               sigma=0.5, seed=1004),
+    "prefill_8k_d128_gqa4": Workload("prefill_8k_d128_gqa4", 1, 32, 8192, 128, "bf16",
+                                     "causal", seed=1005, Hkv=8),
 }
 
 
 def make_inputs(B: int, H: int, S: int, d: int, dtype: str, seed: int,
-                sigma: float = 1.0, outliers: bool = False):
-    """Return (q, k, v) as contiguous CPU torch tensors of ``dtype``."""
+                sigma: float = 1.0, outliers: bool = False, Hkv: int | None = None):
+    """Return (q, k, v) as contiguous CPU torch tensors of ``dtype``; k and v
+    have ``Hkv`` heads (default H)."""
+    Hkv = Hkv or H
     rng = np.random.Generator(np.random.PCG64(seed))
-    shape = (B, H, S, d)
     arrs = []
-    for _ in range(3):
+    for shape in ((B, H, S, d), (B, Hkv, S, d), (B, Hkv, S, d)):
         x = rng.standard_normal(shape, dtype=np.float32)
         if sigma != 1.0:
             x *= np.float32(sigma)
@@ -109,7 +121,7 @@ def make_inputs(B: int, H: int, S: int, d: int, dtype: str, seed: int,
         n_out = int(math.floor(0.01 * S))
         kx = arrs[1]
         for b in range(B):
-            for h in range(H):
+            for h in range(Hkv):
                 idx = rng.choice(S, n_out, replace=False)
                 kx[b, h, idx, :] *= np.float32(8.0)
     tdt = TORCH_DTYPES[dtype]
@@ -117,7 +129,7 @@ def make_inputs(B: int, H: int, S: int, d: int, dtype: str, seed: int,
 
 
 def generate(w: Workload):
-    return make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers)
+    return make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers, w.kv_heads)
 
 
 def input_digest(*tensors) -> str:
