@@ -3,8 +3,9 @@
 Only the tests, the package smoke check and the benchmark's CPU-baseline leg
 may import this package; the product path never does.
 """
-from .attention import (attention_probs_ref, attention_ref, attention_rows_ref,
-                        attention_tiled_ref, kv_head, visible)
+from .attention import (attention_bwd_ref, attention_bwd_rows_ref, attention_probs_ref,
+                        attention_ref, attention_rows_ref, attention_tiled_ref, kv_head,
+                        visible)
 
-__all__ = ["attention_probs_ref", "attention_ref", "attention_rows_ref",
-           "attention_tiled_ref", "kv_head", "visible"]
+__all__ = ["attention_bwd_ref", "attention_bwd_rows_ref", "attention_probs_ref",
+           "attention_ref", "attention_rows_ref", "attention_tiled_ref", "kv_head", "visible"]

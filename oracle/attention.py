@@ -39,6 +39,11 @@ A row with no visible key (not reachable through the library, whose masks
 always keep the diagonal) gets O = 0 and LSE = -inf; the foundry page's
 "Failure modes" section names such rows as the NaN hazard to guard.
 
+Gradients (``attention_bwd_ref``): the Dev.to article's section "The backward
+pass: recompute instead of storing" gives dV = P^T dO, dP = dO V^T, dS from
+the softmax Jacobian applied to dP, and dQ, dK by the matrix-product rules;
+here P is simply materialised, since the oracle is the plain definition.
+
 Grouped key/value heads: the Dev.to article's section "Using it in practice"
 says later variants of the method support grouped-query attention without
 spelling it out.  The plain reading, taken here, is the usual one: K and V
@@ -56,7 +61,7 @@ import math
 import numpy as np
 
 __all__ = ["visible", "attention_ref", "attention_probs_ref", "attention_tiled_ref",
-           "attention_rows_ref", "kv_head"]
+           "attention_rows_ref", "kv_head", "attention_bwd_rows_ref", "attention_bwd_ref"]
 
 _MASKS = ("none", "causal", "window")
 
@@ -223,3 +228,62 @@ def attention_tiled_ref(q, k, v, mask="none", window=None, scale=None, block=64,
     with np.errstate(divide="ignore"):
         lse = np.where(dead, -np.inf, m + np.log(np.where(dead, 1.0, l)))
     return o, lse
+
+
+def attention_bwd_rows_ref(q, k, v, do, mask="none", window=None, scale=None):
+    """Exact fp64 gradients of one head's attention, from the plain definition.
+
+    q, k, v, do: [S, d] (do is the gradient of the loss with respect to O).
+    Returns (dQ, dK, dV), each [S, d] fp64.
+
+    The steps follow the Dev.to article's section "The backward pass: recompute
+    instead of storing": with P the (materialised) softmax probabilities,
+        dV = P^T dO,
+        dP = dO V^T,
+        dS = the softmax Jacobian applied to dP, row by row:
+             dS[i, j] = P[i, j] * (dP[i, j] - sum_t P[i, t] dP[i, t]),
+        dQ = scale * dS K,   dK = scale * dS^T Q
+    (the last two are the matrix-product rules through S = scale * Q K^T).
+    A row with no visible key has P = 0 and contributes nothing.
+    """
+    q, k, v, do = (_as_f64(x) for x in (q, k, v, do))
+    S = q.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    rows = np.arange(S)
+    s = scale * (q @ k.T)
+    vis = visible(rows, np.arange(k.shape[0]), mask, window)
+    s = np.where(vis, s, -np.inf)
+    p, _, _ = _softmax_rows(s)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_bwd_ref(q, k, v, do, mask="none", window=None, scale=None, heads=None):
+    """Exact fp64 gradients over [B, H, S, d] (K, V: [B, Hkv, S, d]; the
+    gradient of a shared key/value head sums over its query heads).
+
+    Returns (dQ [B,H,S,d], dK [B,Hkv,S,d], dV [B,Hkv,S,d]).  ``heads``
+    optionally restricts the work to a list of (b, h) query heads (their
+    contributions only; untouched entries of dQ are NaN).
+    """
+    q, k, v, do = (_as_f64(x) for x in (q, k, v, do))
+    B, H, S, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, d) or v.shape[:3] != (B, Hkv, S) or do.shape[:3] != (B, H, S):
+        raise ValueError("q, k, v, do shapes disagree")
+    dq = np.full(q.shape, np.nan)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        g = kv_head(h, H, Hkv)
+        dq[b, h], dk_h, dv_h = attention_bwd_rows_ref(q[b, h], k[b, g], v[b, g], do[b, h],
+                                                      mask, window, scale)
+        dk[b, g] += dk_h
+        dv[b, g] += dv_h
+    return dq, dk, dv
