@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (forward and
+ * backward passes).
  *
  * The operation is exact attention O = softmax(scale * Q K^T) V evaluated tile
  * by tile with the online softmax: a running row maximum m, a running
@@ -114,6 +115,53 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
 fa_status fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
                      int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t d, int dtype,
                      int mask, int64_t window, float scale, void *stream);
+
+/*
+ * fa_bwd -- gradients of the attention forward pass (fa_fwd / fa_fwd_gqa with
+ * the same q, k, v, B, H, Hkv, S, d, dtype, mask, window and scale) with
+ * respect to q, k and v, given the gradient dout of its output.  The method is
+ * the one in the Dev.to article "FlashAttention: Why Tiling Attention Makes
+ * Transformers Fast Without Changing the Result", section "The backward pass:
+ * recompute instead of storing": the probabilities are recomputed tile by tile
+ * from q, k and the stored logsumexp, never stored, and
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = dO_i . O_i,
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * with P and dS restricted to the visible keys of the mask.  With grouped
+ * key/value heads, dK and dV of key/value head g sum the contributions of its
+ * H / Hkv query heads.
+ *
+ * q, dout : device, [B, H, S, d] contiguous, `dtype`.  Read only.
+ * k, v    : device, [B, Hkv, S, d] contiguous, `dtype`.  Read only.
+ * o, lse  : device; the forward pass's outputs for these arguments (o
+ *           [B, H, S, d] `dtype`, lse [B, H, S] fp32).  Read only.  The
+ *           gradients are those of the forward whose logsumexp is `lse`:
+ *           pass the pair fa_fwd wrote.
+ * dq      : device, [B, H, S, d] `dtype`.  Written.
+ * dk, dv  : device, [B, Hkv, S, d] `dtype`.  Written (each element once, no
+ *           accumulation into existing contents).
+ * delta   : device, [B, H, S] fp32 workspace owned by the caller.  Written
+ *           with D_i (fp32) and read back by the later kernels of this call;
+ *           its contents on return are those row terms.
+ * Hkv     : >= 1 and dividing H (Hkv == H: multi-head attention).
+ * Every other argument is read as by fa_fwd.  Supported: FA_F16 / FA_BF16
+ * with d in {64, 128}.  fp32 products are accumulated in fp32 and each
+ * gradient is rounded to nearest-even into `dtype` once, at the end.
+ *
+ * Ownership, stream order and determinism are as for fa_fwd (three kernel
+ * launches on `stream`, no atomics: bit-identical results on every call).
+ * Errors, all checked on the host before any launch:
+ *   FA_EINVAL       a null or not 16-byte-aligned pointer; B, H, Hkv, S or d
+ *                   < 1; Hkv not dividing H; unknown dtype or mask; window <
+ *                   1 with FA_MASK_WINDOW; non-finite scale; any of dq, dk,
+ *                   dv, delta overlapping an input or another of them; byte
+ *                   counts that overflow, or one head larger than 2 GiB.
+ *   FA_EUNSUPPORTED FA_F32, or d outside {64, 128}.
+ *   FA_EHIP         a launch failed; fa_last_error() holds the HIP message.
+ */
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                 const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B,
+                 int64_t H, int64_t Hkv, int64_t S, int64_t d, int dtype, int mask,
+                 int64_t window, float scale, void *stream);
 
 /*
  * fa_query -- name the kernel instance fa_fwd would launch for (d, dtype,

@@ -1,10 +1,12 @@
-"""MI355X (gfx950) exact-attention forward: Python binding of ``libfa.so``.
+"""MI355X (gfx950) exact attention, forward and backward: Python binding of
+``libfa.so``.
 
-The functions ``fa_fwd``, ``fa_fwd_gqa``, ``fa_query``, ``fa_status_str``,
-``fa_last_error`` and ``fa_abi_version`` mirror the C ABI declared in
-``include/fa.h`` one to one (argument marshalling only).  ``forward`` is the tensor-level convenience
-wrapper: it checks the tensors, allocates ``o`` and ``lse`` with torch and
-launches on torch's current stream.  Every arithmetic step runs in the HIP
+The functions ``fa_fwd``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_query``,
+``fa_status_str``, ``fa_last_error`` and ``fa_abi_version`` mirror the C ABI
+declared in ``include/fa.h`` one to one (argument marshalling only).
+``forward`` and ``backward`` are the tensor-level convenience wrappers: they
+check the tensors, allocate the outputs with torch and launch on torch's
+current stream.  Every arithmetic step runs in the HIP
 kernels; there is no Python or CPU fallback, and a missing library is an
 error.
 """
@@ -14,8 +16,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_gqa", "fa_query", "fa_status_str", "fa_last_error",
-           "fa_abi_version", "forward", "library_path", "DTYPES", "MASKS",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_query", "fa_status_str", "fa_last_error",
+           "fa_abi_version", "forward", "backward", "library_path", "DTYPES", "MASKS",
            "FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
 
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
@@ -55,6 +57,9 @@ def _load():
     lib.fa_fwd_gqa.argtypes = [ctypes.c_void_p] * 5 + [i64] * 5 + [c_int, c_int, i64,
                                                                    ctypes.c_float,
                                                                    ctypes.c_void_p]
+    lib.fa_bwd.restype = c_int
+    lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [i64] * 5 + [c_int, c_int, i64,
+                                                                ctypes.c_float, ctypes.c_void_p]
     lib.fa_query.restype = c_int
     lib.fa_query.argtypes = [i64, c_int, c_int, ctypes.c_char_p, ctypes.c_size_t]
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -91,6 +96,14 @@ def fa_fwd_gqa(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Hkv: in
     """Raw launch with Hkv key/value heads; returns the fa_status code."""
     return _load().fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, S, d, dtype, mask, window,
                               ctypes.c_float(scale), stream)
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,
+           delta: int, B: int, H: int, Hkv: int, S: int, d: int, dtype: int, mask: int,
+           window: int, scale: float, stream: int | None) -> int:
+    """Raw backward launch on device pointers; returns the fa_status code."""
+    return _load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, S, d, dtype,
+                          mask, window, ctypes.c_float(scale), stream)
 
 
 def fa_query(d: int, dtype: int, mask: int) -> str:
@@ -175,3 +188,49 @@ def forward(q, k, v, mask: str = "none", window: int | None = None,
     if st != FA_OK:
         raise FaError(st, fa_last_error())
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, mask: str = "none", window: int | None = None,
+             scale: float | None = None, stream=None):
+    """Gradients (dq, dk, dv) of ``forward(q, k, v, mask, window, scale)``.
+
+    ``o`` and ``lse`` are that forward's outputs and ``dout`` the gradient of
+    ``o``.  dq has q's shape, dk and dv have k's ([B, Hkv, S, d]; with grouped
+    heads they sum over the query heads of each group).  Asynchronous on
+    ``stream`` or torch's current stream.
+    """
+    import torch
+    if mask not in MASKS:
+        raise FaError(FA_EINVAL, f"unknown mask {mask!r}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise FaError(FA_EINVAL, f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise FaError(FA_EINVAL, f"{name} must be a contiguous [B, H, S, d] tensor")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise FaError(FA_EINVAL, f"{name} must match q's dtype and device")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2:] != k.shape[2:]:
+        raise FaError(FA_EINVAL, "k and v must be [B, Hkv, S, d] with q's B, S and d")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise FaError(FA_EINVAL, "o and dout must have q's shape")
+    B, H, S, d = q.shape
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, H, S)
+            or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device):
+        raise FaError(FA_EINVAL, "lse must be a contiguous fp32 [B, H, S] device tensor")
+    dt = _torch_dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    delta.data_ptr(), B, H, k.shape[1], S, d, dt, MASKS[mask],
+                    int(window or 0), float(scale), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return dq, dk, dv

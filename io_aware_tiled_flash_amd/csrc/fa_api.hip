@@ -1,4 +1,4 @@
-// C ABI of the attention forward library: argument validation, choice of the
+// C ABI of the attention library (forward and backward): argument validation, choice of the
 // kernel instance, launch, and per-thread error text.
 //
 // Unsupported requests are errors, never a silent switch to a slower path:
@@ -136,6 +136,103 @@ fa_status fwd_impl(const char *name, const void *q, const void *k, const void *v
   return FA_OK;
 }
 
+// The backward pass (gradients of the forward pass with the same
+// arguments); Hkv == H is plain multi-head attention.
+fa_status bwd_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B,
+                   int64_t H, int64_t Hkv, int64_t S, int64_t d, int dtype, int mask,
+                   int64_t window, float scale, void *stream) {
+  g_err[0] = '\0';
+  const void *ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, delta};
+  for (int i = 0; i < 10; ++i) {
+    if (!ptrs[i]) return fail(FA_EINVAL, "null pointer argument %d", i);
+    if ((uintptr_t)ptrs[i] % 16 != 0)
+      return fail(FA_EINVAL, "pointer argument %d is not 16-byte aligned", i);
+  }
+  if (B < 1 || H < 1 || Hkv < 1 || S < 1 || d < 1)
+    return fail(FA_EINVAL, "sizes must be >= 1 (B=%lld H=%lld Hkv=%lld S=%lld d=%lld)",
+                (long long)B, (long long)H, (long long)Hkv, (long long)S, (long long)d);
+  if (H % Hkv != 0)
+    return fail(FA_EINVAL, "key/value heads (%lld) must divide query heads (%lld)",
+                (long long)Hkv, (long long)H);
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_EINVAL, "unknown dtype %d", dtype);
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_WINDOW)
+    return fail(FA_EINVAL, "unknown mask %d", mask);
+  if (mask == FA_MASK_WINDOW && window < 1)
+    return fail(FA_EINVAL, "window must be >= 1 for the sliding-window mask (got %lld)",
+                (long long)window);
+  if (!isfinite(scale)) return fail(FA_EINVAL, "scale must be finite");
+
+  const int64_t esz = dtype == FA_F32 ? 4 : 2;
+  int64_t bh, rows, elems, bytes, row_bytes, head_bytes, stat_bytes, bhkv, kv_bytes;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, S, &rows) || !mul_ok(rows, d, &elems) ||
+      !mul_ok(elems, esz, &bytes) || !mul_ok(rows, 4, &stat_bytes) ||
+      !mul_ok(d, esz, &row_bytes) || !mul_ok(S, row_bytes, &head_bytes) ||
+      !mul_ok(B, Hkv, &bhkv) || !mul_ok(bhkv, head_bytes, &kv_bytes))
+    return fail(FA_EINVAL, "tensor size overflows 64-bit byte counts");
+  if (head_bytes > (int64_t)INT32_MAX)
+    return fail(FA_EINVAL, "one head's [S, d] slab (%lld bytes) exceeds 2 GiB",
+                (long long)head_bytes);
+  if (bh > (int64_t)INT32_MAX) return fail(FA_EINVAL, "batch*heads too large");
+  // Written buffers may overlap neither each other nor any input.
+  const void *outs[4] = {dq, dk, dv, delta};
+  const int64_t out_n[4] = {bytes, kv_bytes, kv_bytes, stat_bytes};
+  const void *ins[6] = {q, k, v, o, lse, dout};
+  const int64_t in_n[6] = {bytes, kv_bytes, kv_bytes, bytes, stat_bytes, bytes};
+  static const char *out_names[4] = {"dq", "dk", "dv", "delta"};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_n[i], ins[j], in_n[j]))
+        return fail(FA_EINVAL, "output %s overlaps an input", out_names[i]);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_n[i], outs[j], out_n[j]))
+        return fail(FA_EINVAL, "outputs %s and %s overlap", out_names[i], out_names[j]);
+  }
+
+  int eff_mask = mask;
+  if (mask == FA_MASK_WINDOW && window >= S) eff_mask = FA_MASK_CAUSAL;
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = delta;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.Hkv = (int)Hkv;
+  a.S = (int)S;
+  a.window = eff_mask == FA_MASK_WINDOW ? (int)window : 0;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+
+  fa::LaunchInfo info = {nullptr, 0, 0};
+  hipError_t err = hipSuccess;
+  const fa::DType dt = dtype == FA_BF16 ? fa::kBF16 : fa::kF16;
+  if (dtype == FA_F32 || !fa::mfma_backward(dt, (int)d, eff_mask, &a, nullptr, false, &info, &err))
+    return fail(FA_EUNSUPPORTED, "no backward kernel for dtype=%s d=%lld (supported: bf16/f16 "
+                "with d in {64,128})", dtype_name(dtype), (long long)d);
+  const int64_t nt = (S + info.block_rows - 1) / info.block_rows;
+  if (nt * bh > (int64_t)INT32_MAX || rows / 16 + 1 > (int64_t)INT32_MAX)
+    return fail(FA_EINVAL, "grid too large");
+
+  if (log_enabled())
+    fprintf(stderr, "fa_bwd: kernel=%s tiles=%lld block=%d B=%lld H=%lld Hkv=%lld S=%lld d=%lld\n",
+            info.name, (long long)nt, info.threads, (long long)B, (long long)H, (long long)Hkv,
+            (long long)S, (long long)d);
+
+  fa::mfma_backward(dt, (int)d, eff_mask, &a, (hipStream_t)stream, true, &info, &err);
+  if (err != hipSuccess)
+    return fail(FA_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -152,6 +249,14 @@ fa_status fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float
                      int mask, int64_t window, float scale, void *stream) {
   return fwd_impl("fa_fwd_gqa", q, k, v, o, lse, B, H, Hkv, S, d, dtype, mask, window, scale,
                   stream);
+}
+
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                 const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B,
+                 int64_t H, int64_t Hkv, int64_t S, int64_t d, int dtype, int mask,
+                 int64_t window, float scale, void *stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, S, d, dtype, mask, window,
+                  scale, stream);
 }
 
 fa_status fa_query(int64_t d, int dtype, int mask, char *kernel_name, size_t len) {

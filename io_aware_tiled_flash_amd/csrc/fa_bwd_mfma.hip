@@ -1,0 +1,486 @@
+// Backward pass of exact attention on gfx950: gradients dQ, dK, dV from Q, K,
+// V, the forward output O, its logsumexp and the output gradient dO.
+//
+// The method is the one in "FlashAttention: Why Tiling Attention Makes
+// Transformers Fast Without Changing the Result" (Dev.to), section "The
+// backward pass: recompute instead of storing": nothing of size S x S is
+// stored; every score block is recomputed on chip from Q and K, its
+// probabilities are rebuilt from the stored row statistic (P = exp(scale *
+// q.k - LSE), exact because LSE is the final normaliser), and
+//   dV = P^T dO,   dP = dO V^T,
+//   dS = P * (dP - D) with D[i] = dO_i . O_i  (the softmax Jacobian's row
+//        term: sum_j P_ij dP_ij = dO_i . (sum_j P_ij V_j) = dO_i . O_i),
+//   dQ = scale * dS K,   dK = scale * dS^T Q
+// are accumulated tile by tile.
+//
+// Three launches, all deterministic (no atomics):
+//   * row terms: D[i] = dO_i . O_i into a caller-provided fp32 buffer;
+//   * dK/dV: one work-group per 128 keys of one key/value head; each wave
+//     owns 32 keys, keeps their K and V rows in registers as MFMA operands
+//     and streams the query tiles (Q, dO, LSE, D through LDS) of every query
+//     head that reads this key/value head;
+//   * dQ: one work-group per 128 query rows; each wave owns 32 rows, keeps
+//     their Q and dO rows in registers and streams K/V tiles through LDS, as
+//     the forward kernel does.
+// The MFMA layouts are the forward kernel's: score blocks come out of
+// v_mfma_f32_32x32x16 so that each lane holds 16 entries of one column, the
+// accumulator of P (or dS) is directly the operand of the next product once
+// packed, and the transposed operands (dO^T, Q^T, K^T) are read with
+// ds_read_b64_tr_b16 from row-major LDS tiles under the same 64-bank swizzle.
+#include "fa_gfx950.h"
+
+#include <math.h>
+#include <stdio.h>
+
+namespace fa {
+namespace {
+
+using namespace tile;
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Per-lane LDS byte offsets of the two operand kinds on a [32 rows][D] tile
+// stored under swz<D> (the forward kernel's decomposition):
+//   * row operand of step ks: row lq, logical chunk 2*ks + lg (ds_read_b128);
+//   * transposed operand of step kk, d block db, part i2: rows
+//     16*kk + 8*i2 + 4*lg + 0..3 of column 32*db + lane%32 (two
+//     ds_read_b64_tr_b16, one per i2).
+template <int D>
+struct TileOffsets {
+  static constexpr int KSW = D >= 128 ? 8 : 4;
+  static constexpr int NVB = D >= 128 ? 8 : 4;
+  int row_base[KSW];
+  int tr_base[NVB];
+  __device__ inline TileOffsets(int lane) {
+    const int lq = lane & 31, lg = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < KSW; ++j) row_base[j] = lq * (D * 2) + 16 * swz<D>(lq, 2 * j + lg);
+    const int tr_row = 4 * lg + ((lane & 15) >> 2);
+    const int tr_c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int j = 0; j < NVB; ++j) {
+      const int r = 8 * (j & 1) + tr_row;
+      tr_base[j] = r * (D * 2) + 16 * swz<D>(r, 4 * (j >> 1) + tr_c) + 8 * (lane & 1);
+    }
+  }
+  __device__ inline u32x4 row_op(const char *tile, int ks) const {
+    return *(const u32x4 *)(tile + row_base[ks % KSW] + 16 * 2 * KSW * (ks / KSW));
+  }
+  __device__ inline u32x4 tr_op(const char *tile, int kk, int db) const {
+    u32x4 op;
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const u32x2 v2 = lds_read_tr16((const FA_LDS void *)(tile + tr_base[2 * (db & 3) + i2] +
+                                                           16 * kk * (D * 2) + 64 * (db & ~3)));
+      op[2 * i2] = v2[0];
+      op[2 * i2 + 1] = v2[1];
+    }
+    return op;
+  }
+};
+
+// Direct loads of a [32 rows][D] tile (rows row0.., of one head's slab) into
+// an LDS tile, this wave's share: chunk position p of the tile holds row
+// p / KCH, logical chunk c with swz(row, c) == p % KCH.
+template <int D, int NW>
+__device__ inline void load_rows_tile(u32x4 rsrc, int row0, u32x4 *lds_tile, int wave,
+                                      int lane) {
+  constexpr int KCH = D / 8, CHUNKS = 32 * KCH, LPW = CHUNKS / 64 / NW;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int blk = wave * LPW + i;
+    const int pos = 64 * blk + lane;
+    const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
+    load16_to_lds(rsrc, (uint32_t)((row0 + r) * D + 8 * cc) * 2u,
+                  (uint32_t)(uintptr_t)&lds_tile[64 * blk]);
+  }
+}
+
+// Store a transposed accumulator (lane: one column index `col` of the
+// output rows, registers: d values 32*db + 8*(r/4) + 4*lg + (r%4)) as the
+// row `col` of a [rows][D] slab, RNE to the element type.
+template <class Ty, int D>
+__device__ inline void store_rowmajor(uint16_t *row_ptr, const f32x16 (&acc)[D / 32], float mul,
+                                      int lg) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 w;
+      w[0] = Ty::pack2(acc[db][4 * j + 0] * mul, acc[db][4 * j + 1] * mul);
+      w[1] = Ty::pack2(acc[db][4 * j + 2] * mul, acc[db][4 * j + 3] * mul);
+      *(u32x2 *)(row_ptr + 32 * db + 8 * j + 4 * lg) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row terms: D[i] = sum_t dO[i, t] * O[i, t] (fp32), D/8 lanes per row.
+template <class Ty, int D>
+__global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int64_t rows = (int64_t)a.B * a.H * a.S;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+  const int c = tid % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = *(const u32x4 *)((const uint16_t *)a.o + row * D + 8 * c);
+    const u32x4 g = *(const u32x4 *)((const uint16_t *)a.dout + row * D + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x2 ov = Ty::unpack2(o[j]), gv = Ty::unpack2(g[j]);
+      acc = fmaf(ov[0], gv[0], fmaf(ov[1], gv[1], acc));
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && c == 0) a.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV: one work-group per 32*NW keys of one key/value head.
+template <class Ty, int D, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BKV = 32 * NW;  // keys per work-group
+  constexpr int BQ = 32;        // query rows per streamed tile
+  constexpr int NKS = D / 16, NDB = D / 32, KCH = D / 8;
+  constexpr int TILE_CHUNKS = BQ * KCH;
+  static_assert(TILE_CHUNKS % (64 * NW) == 0, "tile must split evenly over the waves");
+  __shared__ u32x4 q_lds[2][TILE_CHUNKS];
+  __shared__ u32x4 do_lds[2][TILE_CHUNKS];
+  __shared__ float lse_lds[2][64];
+  __shared__ float dl_lds[2][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, lg = lane >> 5;
+  const int S = a.S, H = a.H, Hkv = a.Hkv, group = H / Hkv;
+  const int n_kv = a.B * Hkv;
+  const int kvi = blockIdx.x % n_kv;  // key/value head (b * Hkv + hk)
+  const int kt = blockIdx.x / n_kv;   // key tile; the first ones see the most rows
+  const int b = kvi / Hkv, hk = kvi - b * Hkv;
+  const int k0 = kt * BKV, kw0 = k0 + 32 * wave;  // first key of the work-group, of the wave
+  const float c = a.scale_log2;
+
+  const size_t kv_off = (size_t)kvi * (size_t)S * D;
+  const uint32_t head_bytes = (uint32_t)S * D * 2u;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t *)a.k + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t *)a.v + kv_off, head_bytes);
+  // This wave's keys as the B operand of S = Q K^T and dP = dO V^T: lane
+  // (key kw0 + lq, group lg) holds row chunk 2*ks + lg of K and V.
+  u32x4 kreg[NKS], vreg[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const uint32_t off = (uint32_t)((kw0 + lq) * D + 16 * ks + 8 * lg) * 2u;
+    kreg[ks] = load16(rk, off);
+    vreg[ks] = load16(rv, off);
+  }
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(kreg[ks]), "+a"(vreg[ks]));
+
+  // Query tiles that can see a key of this work-group.
+  const int nqt_all = (S + BQ - 1) / BQ;
+  int qt_begin = 0, qt_end = nqt_all;
+  if (MASK != kMaskNone) qt_begin = k0 / BQ;  // rows i >= key
+  if (MASK == kMaskWindow) {
+    const int last_row = min(S - 1, k0 + BKV - 1 + a.window - 1);  // i < key + window
+    qt_end = min(qt_end, last_row / BQ + 1);
+  }
+  const int nq = max(qt_end - qt_begin, 0);
+  const int total = group * nq;  // (query head of the group, query tile) pairs
+
+  const TileOffsets<D> off(lane);
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dkacc[i] = dvacc[i] = f32x16{};
+
+  auto pair_of = [&](int u, int &bh, int &row0) __attribute__((always_inline)) {
+    const int j = u / nq;
+    bh = b * H + hk * group + j;
+    row0 = (qt_begin + u - j * nq) * BQ;
+  };
+  auto issue_loads = [&](int u, int st) __attribute__((always_inline)) {
+    int bh, row0;
+    pair_of(u, bh, row0);
+    const size_t q_off = (size_t)bh * (size_t)S * D;
+    load_rows_tile<D, NW>(rsrc_words((const uint16_t *)a.q + q_off, head_bytes), row0,
+                          q_lds[st], wave, lane);
+    load_rows_tile<D, NW>(rsrc_words((const uint16_t *)a.dout + q_off, head_bytes), row0,
+                          do_lds[st], wave, lane);
+    if (wave == 0)
+      load4_to_lds(rsrc_words(a.lse + (size_t)bh * S, (uint32_t)S * 4u),
+                   (uint32_t)(row0 + lane) * 4u, (uint32_t)(uintptr_t)&lse_lds[st][0]);
+    if (wave == 1)
+      load4_to_lds(rsrc_words(a.delta + (size_t)bh * S, (uint32_t)S * 4u),
+                   (uint32_t)(row0 + lane) * 4u, (uint32_t)(uintptr_t)&dl_lds[st][0]);
+  };
+
+  // Settle the bookkeeping of the kernel-argument scalar loads before the
+  // loop (see the forward kernel): otherwise every load statement in it
+  // waits for lgkmcnt(0).
+  asm volatile("" ::"s"(a.q), "s"(a.dout), "s"(a.lse), "s"(a.delta));
+  if (total > 0) issue_loads(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+
+  for (int u = 0; u < total; ++u) {
+    const int st = u & 1;
+    if (u + 1 < total) issue_loads(u + 1, st ^ 1);
+    int bh, row0;
+    pair_of(u, bh, row0);
+    (void)bh;
+    // Rows of this tile that see none of this wave's keys: skip the math.
+    bool any_visible = row0 < S;
+    if (MASK != kMaskNone) any_visible = any_visible && row0 + BQ - 1 >= kw0;
+    if (MASK == kMaskWindow) any_visible = any_visible && row0 <= kw0 + 31 + a.window - 1;
+    if (any_visible) {
+      const char *qt = (const char *)&q_lds[st][0];
+      const char *dot = (const char *)&do_lds[st][0];
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        sacc = Ty::mfma(off.row_op(qt, ks), kreg[ks], sacc);
+        dpacc = Ty::mfma(off.row_op(dot, ks), vreg[ks], dpacc);
+      }
+      // S accumulator: lane (key kw0 + lq), register r -> row
+      // row0 + 8*(r/4) + 4*lg + (r%4).
+      const bool edge = MASK != kMaskNone ? (row0 < kw0 + 31 || (MASK == kMaskWindow &&
+                                                               row0 + BQ - 1 > kw0 - 1 + a.window))
+                                          : false;
+      const bool tail = row0 + BQ > S || kw0 + 31 >= S;
+      float p[16], ds[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 l4 = *(const float4 *)&lse_lds[st][8 * q4 + 4 * lg];
+        const float4 d4 = *(const float4 *)&dl_lds[st][8 * q4 + 4 * lg];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * q4 + i;
+          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lv[i] * LOG2E));
+          if (edge || tail) {
+            const int row = row0 + 8 * q4 + 4 * lg + i, key = kw0 + lq;
+            bool vis = row < S && key < S;
+            if (MASK == kMaskCausal) vis = vis && key <= row;
+            if (MASK == kMaskWindow) vis = vis && key <= row && key > row - a.window;
+            if (!vis) pr = 0.f;
+          }
+          p[r] = pr;
+          ds[r] = pr * (dpacc[r] - dv[i]);
+        }
+      }
+      u32x4 ppk[2], dspk[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ppk[kk][j] = Ty::pack2(p[8 * kk + 2 * j], p[8 * kk + 2 * j + 1]);
+          dspk[kk][j] = Ty::pack2(ds[8 * kk + 2 * j], ds[8 * kk + 2 * j + 1]);
+        }
+      // dV^T += dO^T P and dK^T += Q^T dS (the transposed tile reads give
+      // rows 16*kk + 8*i2 + 4*lg + 0..3, the order of the packed operands).
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dvacc[db] = Ty::mfma(off.tr_op(dot, kk, db), ppk[kk], dvacc[db]);
+          dkacc[db] = Ty::mfma(off.tr_op(qt, kk, db), dspk[kk], dkacc[db]);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // dK = scale * dS^T Q; each lane holds d values of key kw0 + lq.
+  const int key = kw0 + lq;
+  if (key < S) {
+    store_rowmajor<Ty, D>((uint16_t *)a.dk + kv_off + (size_t)key * D, dkacc, a.scale, lg);
+    store_rowmajor<Ty, D>((uint16_t *)a.dv + kv_off + (size_t)key * D, dvacc, 1.f, lg);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one work-group per 32*NW query rows of one query head.
+template <class Ty, int D, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
+  constexpr int BR = 32 * NW;  // query rows per work-group
+  constexpr int BC = 32;       // keys per streamed tile
+  constexpr int NKS = D / 16, NDB = D / 32, KCH = D / 8;
+  constexpr int TILE_CHUNKS = BC * KCH;
+  static_assert(TILE_CHUNKS % (64 * NW) == 0, "tile must split evenly over the waves");
+  __shared__ u32x4 k_lds[2][TILE_CHUNKS];
+  __shared__ u32x4 v_lds[2][TILE_CHUNKS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, lg = lane >> 5;
+  const int S = a.S;
+  const int BH = a.B * a.H;
+  const int nqt = (S + BR - 1) / BR;
+  const HeadPair hp = head_of_slot(blockIdx.x % BH, a.B, a.H, a.Hkv);
+  int qt = blockIdx.x / BH;
+  if (MASK != kMaskNone) qt = nqt - 1 - qt;  // heaviest query tiles first
+  const int q0 = qt * BR, wr0 = q0 + 32 * wave, wr1 = wr0 + 31;
+  const int row = wr0 + lq;  // this lane's query row
+  const float c = a.scale_log2;
+
+  const size_t q_off = (size_t)hp.q * (size_t)S * D, kv_off = (size_t)hp.kv * (size_t)S * D;
+  const uint32_t head_bytes = (uint32_t)S * D * 2u;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t *)a.q + q_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const uint16_t *)a.dout + q_off, head_bytes);
+  const u32x4 rk = rsrc_words((const uint16_t *)a.k + kv_off, head_bytes);
+  const u32x4 rv = rsrc_words((const uint16_t *)a.v + kv_off, head_bytes);
+  // This wave's rows as the B operand of S^T = K Q^T and dP^T = V dO^T.
+  u32x4 qreg[NKS], doreg[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const uint32_t o = (uint32_t)(row * D + 16 * ks + 8 * lg) * 2u;
+    qreg[ks] = load16(rq, o);
+    doreg[ks] = load16(rdo, o);
+  }
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qreg[ks]), "+a"(doreg[ks]));
+  const float lse2 = row < S ? a.lse[(size_t)hp.q * S + row] * LOG2E : 0.f;
+  const float drow = row < S ? a.delta[(size_t)hp.q * S + row] : 0.f;
+
+  // Key tiles this work-group visits (as in the forward pass).
+  const int ntk = (S + BC - 1) / BC;
+  int kt_begin = 0, kt_end = ntk;
+  if (MASK != kMaskNone) {
+    kt_end = (min(q0 + BR, S) - 1) / BC + 1;
+    if (MASK == kMaskWindow) kt_begin = max(0, q0 - a.window + 1) / BC;
+  }
+
+  const TileOffsets<D> off(lane);
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
+
+  auto issue_loads = [&](int kt, int st) __attribute__((always_inline)) {
+    load_rows_tile<D, NW>(rk, kt * BC, k_lds[st], wave, lane);
+    load_rows_tile<D, NW>(rv, kt * BC, v_lds[st], wave, lane);
+  };
+
+  asm volatile("" ::"s"(rk), "s"(rv), "s"(a.dq));
+  if (kt_begin < kt_end) issue_loads(kt_begin, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int st = (kt - kt_begin) & 1;
+    if (kt + 1 < kt_end) issue_loads(kt + 1, st ^ 1);
+    const int k0 = kt * BC;
+    bool any_visible = wr0 < S;
+    if (MASK != kMaskNone) any_visible = any_visible && k0 <= wr1;
+    if (MASK == kMaskWindow) any_visible = any_visible && k0 + BC - 1 > wr0 - a.window;
+    if (any_visible) {
+      const char *kl = (const char *)&k_lds[st][0];
+      const char *vl = (const char *)&v_lds[st][0];
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        sacc = Ty::mfma(off.row_op(kl, ks), qreg[ks], sacc);
+        dpacc = Ty::mfma(off.row_op(vl, ks), doreg[ks], dpacc);
+      }
+      // S^T accumulator: lane (row wr0 + lq), register r -> key
+      // k0 + 8*(r/4) + 4*lg + (r%4).
+      bool edge;
+      if (MASK == kMaskNone)
+        edge = k0 + BC > S;
+      else if (MASK == kMaskCausal)
+        edge = k0 + BC - 1 > wr0;
+      else
+        edge = k0 + BC - 1 > wr0 || k0 <= wr1 - a.window;
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lse2));
+        if (edge) {
+          const int key = k0 + 8 * (r >> 2) + 4 * lg + (r & 3);
+          bool vis = key < S;
+          if (MASK == kMaskCausal) vis = key <= row;
+          if (MASK == kMaskWindow) vis = key <= row && key > row - a.window;
+          if (!vis) pr = 0.f;
+        }
+        ds[r] = pr * (dpacc[r] - drow);
+      }
+      u32x4 dspk[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dspk[kk][j] = Ty::pack2(ds[8 * kk + 2 * j], ds[8 * kk + 2 * j + 1]);
+      // dQ^T += K^T dS^T.
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dqacc[db] = Ty::mfma(off.tr_op(kl, kk, db), dspk[kk], dqacc[db]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
+
+  if (row < S)
+    store_rowmajor<Ty, D>((uint16_t *)a.dq + q_off + (size_t)row * D, dqacc, a.scale, lg);
+}
+
+// ---------------------------------------------------------------------------
+template <class Ty, int D, int MASK>
+bool run_backward(const BwdArgs *a, hipStream_t stream, bool launch, LaunchInfo *info,
+                  hipError_t *err) {
+  constexpr int NW = 4;
+  static char name[96];
+  static const char *mk[3] = {"none", "causal", "window"};
+  snprintf(name, sizeof(name), "fa_bwd_mfma<%s,d%d,%s,bkv%d,bq%d>", Ty::kName, D, mk[MASK],
+           32 * NW, 32 * NW);
+  info->name = name;
+  info->block_rows = 32 * NW;
+  info->threads = NW * 64;
+  if (!launch) return true;
+  BwdArgs args = *a;
+  void *kargs[] = {&args};
+  const int64_t rows = (int64_t)a->B * a->H * a->S;
+  const int rpb = 256 / (D / 8);
+  *err = hipLaunchKernel((const void *)&fa_bwd_delta_kernel<Ty, D>,
+                         dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), kargs, 0, stream);
+  if (*err != hipSuccess) return true;
+  const int nkt = (a->S + 32 * NW - 1) / (32 * NW);
+  *err = hipLaunchKernel((const void *)&fa_bwd_dkdv_kernel<Ty, D, MASK, NW>,
+                         dim3((unsigned)(nkt * a->B * a->Hkv)), dim3(NW * 64), kargs, 0, stream);
+  if (*err != hipSuccess) return true;
+  *err = hipLaunchKernel((const void *)&fa_bwd_dq_kernel<Ty, D, MASK, NW>,
+                         dim3((unsigned)(nkt * a->B * a->H)), dim3(NW * 64), kargs, 0, stream);
+  return true;
+}
+
+template <class Ty, int D>
+bool bwd_by_mask(int mask, const BwdArgs *a, hipStream_t s, bool launch, LaunchInfo *info,
+                 hipError_t *err) {
+  switch (mask) {
+    case kMaskNone: return run_backward<Ty, D, kMaskNone>(a, s, launch, info, err);
+    case kMaskCausal: return run_backward<Ty, D, kMaskCausal>(a, s, launch, info, err);
+    case kMaskWindow: return run_backward<Ty, D, kMaskWindow>(a, s, launch, info, err);
+  }
+  return false;
+}
+
+template <class Ty>
+bool bwd_by_dim(int d, int mask, const BwdArgs *a, hipStream_t s, bool launch, LaunchInfo *info,
+                hipError_t *err) {
+  switch (d) {
+    case 64: return bwd_by_mask<Ty, 64>(mask, a, s, launch, info, err);
+    case 128: return bwd_by_mask<Ty, 128>(mask, a, s, launch, info, err);
+  }
+  return false;
+}
+
+}  // namespace
+
+bool mfma_backward(DType dt, int d, int mask, const BwdArgs *a, hipStream_t stream, bool launch,
+                   LaunchInfo *info, hipError_t *err) {
+  if (dt == kBF16) return bwd_by_dim<TBF16>(d, mask, a, stream, launch, info, err);
+  if (dt == kF16) return bwd_by_dim<TF16>(d, mask, a, stream, launch, info, err);
+  return false;
+}
+
+}  // namespace fa

@@ -21,6 +21,21 @@ struct FwdArgs {
   float scale_log2;        // scale * log2(e): scores are kept in base-2 units
 };
 
+// Arguments of one backward launch, already validated on the host.
+struct BwdArgs {
+  const void *q;           // [B, H, S, d]
+  const void *k, *v;       // [B, Hkv, S, d]
+  const void *o, *dout;    // [B, H, S, d] forward output and its gradient
+  const float *lse;        // [B, H, S] natural-log logsumexp from the forward pass
+  void *dq;                // [B, H, S, d]
+  void *dk, *dv;           // [B, Hkv, S, d]
+  float *delta;            // [B, H, S] workspace: rowsum(dO * O)
+  int B, H, Hkv, S;
+  int window;              // used by the sliding-window instances only
+  float scale;             // the forward's scale (natural units)
+  float scale_log2;        // scale * log2(e)
+};
+
 // Query head (index into the B*H heads of q, o, lse) and key/value head
 // (index into the B*Hkv heads of k, v) served by work-group slot s in
 // [0, B*H).  Query head h of batch b reads key/value head h / (H / Hkv).
@@ -53,5 +68,10 @@ bool mfma_forward(DType dt, int d, int mask, const FwdArgs *a, hipStream_t strea
                   bool launch, LaunchInfo *info, hipError_t *err);
 bool f32_forward(int d, int mask, const FwdArgs *a, hipStream_t stream, bool launch,
                  LaunchInfo *info, hipError_t *err);
+// Backward pass: three launches on `stream` (row terms, dK/dV, dQ).  Returns
+// false when no instance exists for (dtype, d, mask); `info` names the dK/dV
+// kernel.
+bool mfma_backward(DType dt, int d, int mask, const BwdArgs *a, hipStream_t stream,
+                   bool launch, LaunchInfo *info, hipError_t *err);
 
 }  // namespace fa

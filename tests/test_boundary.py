@@ -29,8 +29,8 @@ def _declared_functions():
 
 def test_library_builds_and_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == ["fa_abi_version", "fa_fwd", "fa_fwd_gqa", "fa_last_error", "fa_query",
-                     "fa_status_str"]
+    assert names == ["fa_abi_version", "fa_bwd", "fa_fwd", "fa_fwd_gqa", "fa_last_error",
+                     "fa_query", "fa_status_str"]
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -139,6 +139,62 @@ def test_grouped_heads_overlap_uses_the_key_value_extent():
     assert _call_gqa(o=A + 128 * MB + 64 * 1024, d=96) == fa.FA_EUNSUPPORTED
     assert _call_gqa(H=8, Hkv=8, d=96) == fa.FA_EUNSUPPORTED
     assert _call_gqa(H=8, Hkv=1, d=96) == fa.FA_EUNSUPPORTED
+
+
+def _call_bwd(**kw):
+    # [1, 4, 128, 128] bf16 = 128 KiB per query-shaped tensor, [1, 2, 128, 128]
+    # = 64 KiB per key/value-shaped one, 2 KiB per row statistic.
+    args = dict(q=A, k=A + 16 * MB, v=A + 32 * MB, o=A + 48 * MB, lse=A + 64 * MB,
+                dout=A + 80 * MB, dq=A + 96 * MB, dk=A + 112 * MB, dv=A + 128 * MB,
+                delta=A + 144 * MB, B=1, H=4, Hkv=2, S=128, d=128, dtype=2, mask=1, window=0,
+                scale=0.088, stream=None)
+    args.update(kw)
+    names = ["q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta", "B", "H", "Hkv",
+             "S", "d", "dtype", "mask", "window", "scale", "stream"]
+    return fa.fa_bwd(*[args[n] for n in names])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(q=0), "null"), (dict(dout=0), "null"), (dict(delta=0), "null"), (dict(dv=0), "null"),
+    (dict(dk=A + 112 * MB + 4), "aligned"), (dict(lse=A + 64 * MB + 8), "aligned"),
+    (dict(B=0), "sizes"), (dict(Hkv=0), "sizes"), (dict(S=0), "sizes"), (dict(d=-1), "sizes"),
+    (dict(Hkv=3), "divide"), (dict(dtype=5), "dtype"), (dict(mask=-1), "mask"),
+    (dict(mask=2, window=0), "window"), (dict(scale=float("nan")), "finite"),
+    (dict(dq=A + 16), "dq overlaps an input"),              # inside q
+    (dict(dk=A + 80 * MB + 64 * 1024), "dk overlaps"),      # inside dout
+    (dict(delta=A + 64 * MB + 1024), "delta overlaps"),     # inside lse
+    (dict(dv=A + 112 * MB + 32 * 1024), "dk and dv overlap"),
+    (dict(delta=A + 96 * MB + 64 * 1024), "dq and delta overlap"),
+    (dict(B=1 << 40, H=1 << 30, Hkv=1), "overflow"), (dict(S=1 << 24, d=256), "2 GiB"),
+])
+def test_backward_invalid_arguments_are_rejected_before_any_launch(kw, needle):
+    st = _call_bwd(**kw)
+    assert st == fa.FA_EINVAL, (st, fa.fa_last_error())
+    assert needle in fa.fa_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=0), dict(dtype=0, d=64), dict(d=256),
+                                dict(d=96, dtype=1), dict(d=32)])
+def test_backward_unsupported_configuration_is_an_error(kw):
+    assert _call_bwd(**kw) == fa.FA_EUNSUPPORTED
+    assert "no backward kernel" in fa.fa_last_error()
+
+
+def test_backward_overlap_uses_the_key_value_extent():
+    # k is [1, 2, 128, 96] bf16 (48 KiB; d=96 keeps anything from launching):
+    # a dk right after that extent, but inside where 4 heads would reach, is
+    # accepted, while one that starts inside it is refused.
+    kv = 2 * 128 * 96 * 2
+    assert _call_bwd(dk=A + 16 * MB + kv, d=96) == fa.FA_EUNSUPPORTED
+    assert _call_bwd(dk=A + 16 * MB + kv - 16, d=96) == fa.FA_EINVAL
+
+
+def test_backward_refuses_host_tensors():
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(fa.FaError) as e:
+        fa.backward(q, q, q, q, lse, q, mask="causal")
+    assert e.value.status == fa.FA_EINVAL
 
 
 def test_window_argument_ignored_without_window_mask():

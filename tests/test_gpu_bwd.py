@@ -1,0 +1,158 @@
+"""GPU parity of the backward pass: the HIP kernels' dQ, dK, dV against the
+fp64 oracle's exact gradients on identical seeded inputs.
+
+Bar: every element within the first-order error bound of 16-bit storage with
+fp32 accumulation (tests/bwd_bounds.py derives it; tests/test_bwd_bounds.py
+shows that 16-bit rounding stays inside it and that plausible mistakes do
+not).  The forward output and logsumexp fed to the backward are the HIP
+forward's, as a caller would pass them.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_flash_amd as fa
+from bwd_bounds import excess, grad_bounds
+from workloads import make_grad, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device (run with -m 'not gpu' on a host)")
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _inputs(B, H, Hkv, S, d, dtype, seed):
+    q, k, v = make_inputs(B, H, S, d, dtype, seed, Hkv=Hkv)
+    do = make_grad(B, H, S, d, dtype, seed + 7919)
+    return q, k, v, do
+
+
+def _run(q, k, v, do, mask, window, scale):
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, mask=mask, window=window, scale=scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, mask=mask, window=window, scale=scale)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _check(B, H, Hkv, S, d, dtype, mask, window=None, seed=11, scale=None):
+    label = f"bwd {dtype} d={d} {mask} w={window} B={B} H={H} Hkv={Hkv} S={S} seed={seed}"
+    _say(label)
+    q, k, v, do = _inputs(B, H, Hkv, S, d, dtype, seed)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    got = _run(q, k, v, do, mask, window, scale)
+    ref, bnd = grad_bounds(q, k, v, do, mask, window, scale, dtype)
+    report = []
+    for name, g, r, b in zip(("dq", "dk", "dv"), got, ref, bnd):
+        assert torch.isfinite(g.float()).all(), f"{label}: {name} not finite"
+        x = excess(g, r, b)
+        report.append((name, x, _worst(g, r, b)))
+    _say("  " + "  ".join(f"{n}: {x:.3f} of bound" for n, x, _ in report))
+    for name, x, where in report:
+        assert x <= 1.0, f"{label}: {name} error reaches {x:.3f} of its bound at {where}"
+    return got
+
+
+def _worst(got, ref, bound):
+    err = np.abs(got.double().numpy() - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(err == 0, 0.0, err / bound)
+    i = np.unravel_index(np.nanargmax(r), r.shape)
+    return (f"index {tuple(int(t) for t in i)}: got {float(got[i]):.6g} "
+            f"exact {ref[i]:.6g} bound {bound[i]:.3g}")
+
+
+CASES = [
+    # dtype, d, mask, H, Hkv, S, window
+    ("bf16", 128, "causal", 2, 2, 256, None),   # whole tiles
+    ("bf16", 128, "causal", 2, 2, 300, None),   # ragged tail
+    ("bf16", 64, "causal", 2, 2, 300, None),
+    ("bf16", 128, "none", 2, 2, 200, None),
+    ("bf16", 64, "none", 1, 1, 333, None),
+    ("f16", 128, "none", 1, 1, 333, None),
+    ("f16", 64, "causal", 2, 2, 129, None),
+    ("f16", 128, "causal", 1, 1, 511, None),
+    ("bf16", 128, "window", 2, 2, 700, 100),
+    ("bf16", 64, "window", 1, 1, 513, 33),
+    ("f16", 128, "window", 1, 1, 400, 1),       # window of one: the diagonal only
+    ("bf16", 128, "causal", 8, 2, 300, None),   # grouped heads
+    ("f16", 64, "none", 6, 3, 257, None),
+    ("bf16", 128, "causal", 4, 1, 200, None),   # one shared key/value head
+    ("bf16", 128, "window", 4, 2, 333, 50),
+]
+
+
+@pytest.mark.parametrize("dtype,d,mask,H,Hkv,S,window", CASES)
+def test_backward_full(dtype, d, mask, H, Hkv, S, window):
+    _check(1, H, Hkv, S, d, dtype, mask, window)
+
+
+@pytest.mark.parametrize("S", [1, 2, 31, 32, 33, 127, 128, 129])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_backward_short_sequences(S, mask):
+    _check(1, 2, 2, S, 128, "bf16", mask)
+
+
+def test_backward_batch():
+    _check(3, 2, 1, 190, 64, "bf16", "causal")
+
+
+@pytest.mark.parametrize("scale", [0.02, 1.0, -0.1])
+def test_backward_scale_values(scale):
+    _check(1, 1, 1, 160, 64, "bf16", "causal", scale=scale)
+
+
+def test_backward_window_covering_sequence_is_causal_bitwise():
+    q, k, v, do = _inputs(1, 2, 2, 300, 128, "bf16", 3)
+    a = _run(q, k, v, do, "causal", None, 0.1)
+    b = _run(q, k, v, do, "window", 300, 0.1)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_deterministic_repeat():
+    q, k, v, do = _inputs(1, 4, 2, 400, 128, "bf16", 4)
+    a = _run(q, k, v, do, "causal", None, 0.09)
+    b = _run(q, k, v, do, "causal", None, 0.09)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_outputs_do_not_touch_neighbours():
+    """dq, dk, dv, delta carved out of larger buffers: the guard bytes around
+    each stay untouched."""
+    B, H, Hkv, S, d = 1, 2, 1, 200, 64
+    q, k, v, do = _inputs(B, H, Hkv, S, d, "bf16", 5)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, mask="causal")
+    pad = 4096
+    sizes = [B * H * S * d, B * Hkv * S * d, B * Hkv * S * d]
+    bufs = [torch.full((n + 2 * pad,), 7.0, dtype=torch.bfloat16, device=dev) for n in sizes]
+    dl = torch.full((B * H * S + 2 * pad,), 3.0, dtype=torch.float32, device=dev)
+    ptr = [b.data_ptr() + 2 * pad for b in bufs]
+    st = fa.fa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   dod.data_ptr(), ptr[0], ptr[1], ptr[2], dl.data_ptr() + 4 * pad, B, H, Hkv,
+                   S, d, fa.DTYPES["bf16"], fa.MASKS["causal"], 0, 1.0 / math.sqrt(d),
+                   torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK, fa.fa_last_error()
+    torch.cuda.synchronize()
+    for b, n in zip(bufs, sizes):
+        assert torch.all(b[:pad] == 7.0) and torch.all(b[pad + n:] == 7.0)
+    assert torch.all(dl[:pad] == 3.0) and torch.all(dl[pad + B * H * S:] == 3.0)
+    ref = fa.backward(qd, kd, vd, o, lse, dod, mask="causal")
+    for b, n, r in zip(bufs, sizes, ref):
+        assert torch.equal(b[pad:pad + n].view_as(r), r)

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward pass.
+"""Seeded synthetic inputs for the attention forward and backward passes.
 
 This module is shared by the oracle-side tests and the GPU-side tests and
 benchmark.  It only draws random numbers and rounds them to the storage dtype;
@@ -12,6 +12,9 @@ Recipe (applies to every workload):
     [B, H, S, d] for Q and [B, Hkv, S, d] for K and V (Hkv = H unless the
     workload has grouped key/value heads);
   * rounding: round-to-nearest-even to the storage dtype (torch CPU ``.to``);
+  * output gradient for the backward pass (``make_grad``): its own generator
+    ``PCG64(seed)`` over [B, H, S, d], ``standard_normal`` float32, rounded
+    the same way (callers pass a seed distinct from the inputs' seed);
   * optional outliers: after the three draws, for every (b, h) of K in (b, h)
     order, ``rng.choice(S, floor(0.01 * S), replace=False)`` picks key rows that
     are multiplied by 8 (a power of two, so scaling before or after rounding
@@ -32,7 +35,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "generate", "input_digest",
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_grad", "generate", "input_digest",
            "TORCH_DTYPES"]
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -126,6 +129,13 @@ def make_inputs(B: int, H: int, S: int, d: int, dtype: str, seed: int,
                 kx[b, h, idx, :] *= np.float32(8.0)
     tdt = TORCH_DTYPES[dtype]
     return tuple(torch.from_numpy(a).to(tdt).contiguous() for a in arrs)
+
+
+def make_grad(B: int, H: int, S: int, d: int, dtype: str, seed: int):
+    """The gradient of the output, dO: a contiguous CPU tensor [B, H, S, d]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((B, H, S, d), dtype=np.float32)
+    return torch.from_numpy(x).to(TORCH_DTYPES[dtype]).contiguous()
 
 
 def generate(w: Workload):
