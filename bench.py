@@ -2,6 +2,8 @@
 
 One step is one ``fa_fwd`` launch over the whole batch of the workload (all
 of the hot path: tile loads, QK^T, masking, online softmax, PV, epilogue).
+With ``--pass bwd`` a step is one ``fa_bwd`` call instead (gradients of the
+same workload, given the forward's outputs and a seeded output gradient).
 Inputs are generated once, copied to HBM and reused; W untimed steps, then K
 steps timed with events on the launch stream, bracketed by synchronisation.
 The default W is about a second of work: under sustained MFMA load the
@@ -30,6 +32,12 @@ METRIC = "attention fwd TFLOP/s at S=8K,d=128 bf16 causal; % of MFMA bf16 peak"
 HEADLINE = "prefill_8k_d128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense: MFMA bf16/f16, fp32 vector
 HBM_PEAK_GBS = 8000.0
+# Backward FLOPs: five products of 2*d FLOPs per visible (row, key) pair (S and
+# dP recomputed once, dV, dK, dQ) against the forward's two, the usual
+# accounting; recomputing S and dP a second time for dQ is not counted.
+BWD_FLOP_RATIO = 2.5
+BWD_KERNELS = ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel")
+GRAD_SEED_OFFSET = 7919  # dO is drawn with seed = the workload's seed + this
 CSRC = os.path.join(ROOT, "io_aware_tiled_flash_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -90,6 +98,33 @@ def cpu_baseline(w, q, k, v, target_s: float):
             "seconds": round(el, 2)}
 
 
+def cpu_baseline_bwd(w, q, k, v, do, target_s: float):
+    """Time the fp64 oracle's gradients on whole heads until ~target_s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_bwd_rows_ref
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    per_head_pairs = w.visible_pairs() // (w.B * w.H)
+    group = w.H // w.kv_heads
+    t0 = time.perf_counter()
+    heads = 0
+    while True:
+        b, h = divmod(heads, w.H)
+        g = h // group
+        attention_bwd_rows_ref(q[b, h], k[b, g], v[b, g], do[b, h], w.mask, w.window or None,
+                               w.scale)
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or heads >= w.B * w.H:
+            break
+    flops = BWD_FLOP_RATIO * 4.0 * w.d * per_head_pairs * heads
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"gradients of {heads} of {w.B * w.H} heads of {w.name} (all {w.S} "
+                      f"rows, fp64 numpy, P materialised per head), {el:.1f} s",
+            "seconds": round(el, 2)}
+
+
 def copy_calibration(args) -> int:
     """Plain copy of a known byte count per step, for scaling HBM counters."""
     import torch
@@ -116,6 +151,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward pass (the headline) or the backward pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -132,7 +169,7 @@ def main() -> int:
     import torch
 
     import io_aware_tiled_flash_amd as fa
-    from workloads import WORKLOADS, make_inputs
+    from workloads import WORKLOADS, make_grad, make_inputs
 
     w = WORKLOADS[args.workload]
     if not torch.cuda.is_available():
@@ -152,6 +189,25 @@ def main() -> int:
         fa.forward(q, k, v, mask=w.mask, window=window, scale=w.scale, out=o, lse=lse,
                    stream=stream)
 
+    if args.pass_ == "bwd":
+        # the forward once (untimed) for O and the logsumexp, then the timed
+        # step is one fa_bwd call (all three of its launches)
+        step()
+        dout = make_grad(w.B, w.H, w.S, w.d, w.dtype, w.seed + GRAD_SEED_OFFSET).to(dev)
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        delta = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+        bwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    delta.data_ptr(), w.B, w.H, w.kv_heads, w.S, w.d, fa.DTYPES[w.dtype],
+                    fa.MASKS[w.mask], int(w.window or 0), float(w.scale), stream.cuda_stream)
+
+        def step():  # noqa: F811
+            st = fa.fa_bwd(*bwd_args)
+            if st != fa.FA_OK:
+                raise fa.FaError(st, fa.fa_last_error())
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -164,12 +220,19 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    flops = w.flops()
+    bwd = args.pass_ == "bwd"
+    flops = w.flops() * (BWD_FLOP_RATIO if bwd else 1.0)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(w.name)
-    metric = METRIC if w.name == HEADLINE else (
-        f"attention fwd TFLOP/s on {w.name}; % of MFMA {w.dtype} peak")
+    traffic = None if bwd else measured_traffic(w.name)
+    if bwd:
+        metric = (f"attention bwd TFLOP/s on {w.name} (10*d FLOPs per visible pair); "
+                  f"% of MFMA {w.dtype} peak")
+        kernel = "fa_bwd: " + ", ".join(BWD_KERNELS)
+    else:
+        metric = METRIC if w.name == HEADLINE else (
+            f"attention fwd TFLOP/s on {w.name}; % of MFMA {w.dtype} peak")
+        kernel = fa.fa_query(w.d, fa.DTYPES[w.dtype], fa.MASKS[w.mask])
     result = {
         "metric": metric,
         "value": round(tflops, 2),
@@ -186,7 +249,7 @@ def main() -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "S": w.S,
                    "d": w.d,
                    "mask": w.mask, "window": w.window or None, "input_dtype": w.dtype,
-                   "kernel": fa.fa_query(w.d, fa.DTYPES[w.dtype], fa.MASKS[w.mask])},
+                   "pass": args.pass_, "kernel": kernel},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
@@ -195,8 +258,13 @@ def main() -> int:
                 "compulsory_GBps": round(w.compulsory_bytes() / (ms * 1e-3) / 1e9, 1),
                 "peak_GBps": HBM_PEAK_GBS},
     }
+    if bwd:
+        result["roofline"]["scope"] = "whole pass (three launches)"
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, *host, args.cpu_seconds)
+        if bwd:
+            result["cpu_baseline"] = cpu_baseline_bwd(w, *host, dout.cpu(), args.cpu_seconds)
+        else:
+            result["cpu_baseline"] = cpu_baseline(w, *host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -156,3 +156,59 @@ def test_backward_outputs_do_not_touch_neighbours():
     ref = fa.backward(qd, kd, vd, o, lse, dod, mask="causal")
     for b, n, r in zip(bufs, sizes, ref):
         assert torch.equal(b[pad:pad + n].view_as(r), r)
+
+
+@pytest.mark.parametrize("name", ["prefill_8k_d128"])
+def test_backward_full_size_workload(name):
+    """The benchmark's backward configuration at full size.  Every head:
+    sum_j dV[j] = sum_i dO[i] (each row's probabilities sum to one), within
+    the sum of the per-element bounds, which for this identity needs only dO
+    and dV.  Two whole heads: every element against the oracle within its
+    bound."""
+    from bwd_bounds import UNIT, F32, head_bounds
+    from oracle import attention_bwd_rows_ref
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[name]
+    _say(f"bwd full-size {name}")
+    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers, w.kv_heads)
+    do = make_grad(w.B, w.H, w.S, w.d, w.dtype, w.seed + 7919)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, mask=w.mask, window=w.window or None, scale=w.scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, mask=w.mask, window=w.window or None,
+                             scale=w.scale)
+    torch.cuda.synchronize()
+    dq, dk, dv, lse = dq.cpu(), dk.cpu(), dv.cpu(), lse.cpu()
+    for name_, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.isfinite(t.float()).all(), f"{name_} not finite"
+
+    u = UNIT[w.dtype]
+    g = (w.S + w.d + 16) * F32
+    group = w.H // w.kv_heads
+    qn = q.double().norm(dim=-1).amax().item()
+    kn = k.double().norm(dim=-1).amax().item()
+    rho = g * (abs(w.scale) * qn * kn + 1.0 + lse.abs().max().item() + 1e-3) + 4 * F32
+    do64, dv64 = do.double(), dv.double()
+    for b in range(w.B):
+        for gh in range(w.kv_heads):
+            heads = slice(gh * group, (gh + 1) * group)
+            lhs = dv64[b, gh].sum(dim=0)
+            rhs = do64[b, heads].sum(dim=(0, 1))
+            tol = (u + g + rho) * do64[b, heads].abs().sum(dim=(0, 1)) \
+                + u * dv64[b, gh].abs().sum(dim=0)
+            gap = ((lhs - rhs).abs() / tol).max().item()
+            assert gap <= 1.0, f"kv head {gh}: sum_j dV - sum_i dO reaches {gap:.3f} of bound"
+
+    assert w.kv_heads == w.H, "the whole-head check below assumes one query head per kv head"
+    for h in (0, w.H - 1):
+        _say(f"  head {h}: exact gradients and bounds")
+        args = (q[0, h], k[0, h], v[0, h], do[0, h], w.mask, w.window or None, w.scale)
+        ref = attention_bwd_rows_ref(*args)
+        bnd = head_bounds(*args, w.dtype)
+        for name_, got, r, e in zip(("dq", "dk", "dv"), (dq[0, h], dk[0, h], dv[0, h]), ref,
+                                    bnd):
+            b_ = e + u * np.abs(r)
+            x = excess(got, r, b_)
+            _say(f"  head {h} {name_}: {x:.3f} of bound")
+            assert x <= 1.0, f"head {h}: {name_} error reaches {x:.3f} of its bound"
