@@ -164,6 +164,75 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
                  int64_t window, float scale, void *stream);
 
 /*
+ * fa_decode_paged -- attention of a few new tokens per request over a paged
+ * key/value cache (decoding).  The aicomputerinstitute.com grade-12 chapter on
+ * flash attention, sections "A different bottleneck: the KV cache during
+ * inference" and "PagedAttention: memory management borrowed from an
+ * operating system", describes the layout: the cache is cut into fixed-size
+ * physical blocks stored anywhere, and each request's block table maps its
+ * logical token positions to blocks, which the kernel walks and gathers.
+ *
+ * For request b with n_b = min(max(ctx_lens[b], 0), max_ctx, max_blocks *
+ * block_size) cached tokens:
+ *   token t < n_b lives in physical block P = block_table[b * max_blocks +
+ *   t / block_size], slot t % block_size; a table entry outside
+ *   [0, num_blocks) holds no token (its positions are skipped, never read);
+ *   query row i (0 <= i < n_q) is the token at position n_b - n_q + i, whose
+ *   key and value are already cached, and attends to positions t <= n_b -
+ *   n_q + i (with n_q = 1: every cached token);
+ *   query head h uses key/value head h / (H / Hkv).
+ * O and lse are the exact attention of each row over its visible tokens
+ * (softmax of scale * q.k, as fa_fwd); a row with no visible token gets O = 0
+ * and lse = -inf.
+ *
+ * q, o       : device, [B, H, n_q, d] contiguous, `dtype` (o written).
+ * k_cache, v_cache : device, [num_blocks, Hkv, block_size, d] contiguous,
+ *              `dtype`.  Read only; only the slots of valid tokens are read.
+ * block_table: device int32 [B, max_blocks].   ctx_lens: device int32 [B].
+ * lse        : device fp32 [B, H, n_q] (written, natural log).
+ * workspace, workspace_bytes : device scratch for the partial results of
+ *              long contexts, split over several work-groups and merged; the
+ *              size is given by fa_decode_workspace_size for the same sizes
+ *              (0 when no split is needed: workspace may then be NULL).  Its
+ *              contents are undefined before and after the call.
+ * max_ctx    : an upper bound the caller guarantees for the context lengths
+ *              (host value; it sizes the split and the workspace).  Longer
+ *              contexts are cut to max_ctx tokens.
+ * block_size : a power of two, 1 .. 1024.
+ * Supported: FA_F16 / FA_BF16 with d in {64, 128}.
+ *
+ * Ownership, stream order and determinism as for fa_fwd (one or two launches).
+ * Errors, checked on the host before any launch:
+ *   FA_EINVAL       a null pointer (workspace only when needed); q, caches,
+ *                   o or workspace not 16-byte aligned, block_table, ctx_lens
+ *                   or lse not 4-byte aligned; B, H, Hkv, n_q, d, num_blocks,
+ *                   block_size or max_blocks < 1; max_ctx < 0; Hkv not
+ *                   dividing H; unknown dtype; non-finite scale; workspace
+ *                   smaller than required; o, lse or workspace overlapping an
+ *                   input or each other; sizes beyond the kernels' index range.
+ *   FA_EUNSUPPORTED FA_F32, d outside {64, 128}, or a block_size that is not a
+ *                   power of two up to 1024.
+ *   FA_EHIP         a launch failed.
+ * Values inside block_table and ctx_lens are device data and are never
+ * checked on the host; out-of-range entries are handled as described above.
+ */
+fa_status fa_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_table, const int32_t *ctx_lens, void *o,
+                          float *lse, void *workspace, size_t workspace_bytes, int64_t B,
+                          int64_t H, int64_t Hkv, int64_t n_q, int64_t d, int64_t num_blocks,
+                          int64_t block_size, int64_t max_blocks, int64_t max_ctx, int dtype,
+                          float scale, void *stream);
+
+/*
+ * fa_decode_workspace_size -- bytes of workspace fa_decode_paged needs for
+ * these sizes (written to *bytes; 0 when none).  Same size checks and error
+ * codes as fa_decode_paged; touches no device memory.
+ */
+fa_status fa_decode_workspace_size(int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t d,
+                                   int64_t num_blocks, int64_t block_size, int64_t max_blocks,
+                                   int64_t max_ctx, int dtype, size_t *bytes);
+
+/*
  * fa_query -- name the kernel instance fa_fwd would launch for (d, dtype,
  * mask), without launching anything or touching the GPU.  Writes a
  * NUL-terminated name into kernel_name[0..len) (truncated if needed; may be

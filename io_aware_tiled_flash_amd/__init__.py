@@ -1,10 +1,11 @@
 """MI355X (gfx950) exact attention, forward and backward: Python binding of
 ``libfa.so``.
 
-The functions ``fa_fwd``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_query``,
-``fa_status_str``, ``fa_last_error`` and ``fa_abi_version`` mirror the C ABI
-declared in ``include/fa.h`` one to one (argument marshalling only).
-``forward`` and ``backward`` are the tensor-level convenience wrappers: they
+The functions ``fa_fwd``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_decode_paged``,
+``fa_decode_workspace_size``, ``fa_query``, ``fa_status_str``,
+``fa_last_error`` and ``fa_abi_version`` mirror the C ABI declared in
+``include/fa.h`` one to one (argument marshalling only).  ``forward``,
+``backward`` and ``decode`` are the tensor-level convenience wrappers: they
 check the tensors, allocate the outputs with torch and launch on torch's
 current stream.  Every arithmetic step runs in the HIP
 kernels; there is no Python or CPU fallback, and a missing library is an
@@ -16,8 +17,9 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_query", "fa_status_str", "fa_last_error",
-           "fa_abi_version", "forward", "backward", "library_path", "DTYPES", "MASKS",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_decode_paged",
+           "fa_decode_workspace_size", "fa_query", "fa_status_str", "fa_last_error",
+           "fa_abi_version", "forward", "backward", "decode", "library_path", "DTYPES", "MASKS",
            "FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
 
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
@@ -60,6 +62,11 @@ def _load():
     lib.fa_bwd.restype = c_int
     lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [i64] * 5 + [c_int, c_int, i64,
                                                                 ctypes.c_float, ctypes.c_void_p]
+    lib.fa_decode_paged.restype = c_int
+    lib.fa_decode_paged.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_size_t] + [i64] * 9 +
+                                    [c_int, ctypes.c_float, ctypes.c_void_p])
+    lib.fa_decode_workspace_size.restype = c_int
+    lib.fa_decode_workspace_size.argtypes = [i64] * 9 + [c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_query.restype = c_int
     lib.fa_query.argtypes = [i64, c_int, c_int, ctypes.c_char_p, ctypes.c_size_t]
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -104,6 +111,30 @@ def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int
     """Raw backward launch on device pointers; returns the fa_status code."""
     return _load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, S, d, dtype,
                           mask, window, ctypes.c_float(scale), stream)
+
+
+def fa_decode_paged(q: int, k_cache: int, v_cache: int, block_table: int, ctx_lens: int,
+                    o: int, lse: int, workspace: int | None, workspace_bytes: int, B: int,
+                    H: int, Hkv: int, n_q: int, d: int, num_blocks: int, block_size: int,
+                    max_blocks: int, max_ctx: int, dtype: int, scale: float,
+                    stream: int | None) -> int:
+    """Raw paged-cache decode launch on device pointers; returns the status."""
+    return _load().fa_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, o, lse,
+                                   workspace, workspace_bytes, B, H, Hkv, n_q, d, num_blocks,
+                                   block_size, max_blocks, max_ctx, dtype,
+                                   ctypes.c_float(scale), stream)
+
+
+def fa_decode_workspace_size(B: int, H: int, Hkv: int, n_q: int, d: int, num_blocks: int,
+                             block_size: int, max_blocks: int, max_ctx: int,
+                             dtype: int) -> int:
+    """Workspace bytes fa_decode_paged needs for these sizes (raises on error)."""
+    out = ctypes.c_size_t(0)
+    st = _load().fa_decode_workspace_size(B, H, Hkv, n_q, d, num_blocks, block_size,
+                                          max_blocks, max_ctx, dtype, ctypes.byref(out))
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return out.value
 
 
 def fa_query(d: int, dtype: int, mask: int) -> str:
@@ -234,3 +265,51 @@ def backward(q, k, v, o, lse, dout, mask: str = "none", window: int | None = Non
     if st != FA_OK:
         raise FaError(st, fa_last_error())
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, block_table, ctx_lens, max_ctx: int, scale: float | None = None,
+           stream=None):
+    """Attention of q's n_q newest tokens per request over a paged cache.
+
+    q: [B, H, n_q, d]; k_cache, v_cache: [num_blocks, Hkv, block_size, d];
+    block_table: int32 [B, max_blocks]; ctx_lens: int32 [B]; all on one
+    device.  ``max_ctx`` is a host-side bound on the context lengths.
+    Returns (o [B, H, n_q, d], lse fp32 [B, H, n_q]).
+    """
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("ctx_lens", ctx_lens)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise FaError(FA_EINVAL, f"{name} must be a contiguous device tensor")
+        if t.device != q.device:
+            raise FaError(FA_EINVAL, f"{name} must be on q's device")
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise FaError(FA_EINVAL, "q must be [B, H, n_q, d] and the caches "
+                                 "[num_blocks, Hkv, block_size, d]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise FaError(FA_EINVAL, "q and the caches must share a dtype")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise FaError(FA_EINVAL, "block_table and ctx_lens must be int32")
+    B, H, n_q, d = q.shape
+    nb, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or block_table.dim() != 2 or block_table.shape[0] != B or \
+            ctx_lens.shape != (B,):
+        raise FaError(FA_EINVAL, "shapes of the caches, block_table or ctx_lens disagree with q")
+    dt = _torch_dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mb = block_table.shape[1]
+    ws_bytes = fa_decode_workspace_size(B, H, Hkv, n_q, d, nb, bs, mb, int(max_ctx), dt)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = fa_decode_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                             block_table.data_ptr(), ctx_lens.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), ws.data_ptr(), ws.numel(), B, H, Hkv, n_q, d, nb,
+                             bs, mb, int(max_ctx), dt, float(scale), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return o, lse

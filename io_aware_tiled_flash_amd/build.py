@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_f32.hip", "fa_bwd_mfma.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_f32.hip", "fa_bwd_mfma.hip", "fa_decode.hip"]
 
 # Per-source extra flags for the matrix-core kernel:
 #  * it never produces or consumes NaN (masked scores are -inf, which stays

@@ -233,6 +233,138 @@ fa_status bwd_impl(const void *q, const void *k, const void *v, const void *o, c
   return FA_OK;
 }
 
+// Shared size checks of the decode entry points; fills the plan.
+fa_status decode_sizes(int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t d,
+                       int64_t num_blocks, int64_t block_size, int64_t max_blocks,
+                       int64_t max_ctx, int dtype, int *bs_shift, int64_t *ctx_cap,
+                       fa::DecodePlan *plan) {
+  if (B < 1 || H < 1 || Hkv < 1 || n_q < 1 || d < 1 || num_blocks < 1 || block_size < 1 ||
+      max_blocks < 1)
+    return fail(FA_EINVAL, "sizes must be >= 1 (B=%lld H=%lld Hkv=%lld n_q=%lld d=%lld "
+                "num_blocks=%lld block_size=%lld max_blocks=%lld)", (long long)B, (long long)H,
+                (long long)Hkv, (long long)n_q, (long long)d, (long long)num_blocks,
+                (long long)block_size, (long long)max_blocks);
+  if (max_ctx < 0) return fail(FA_EINVAL, "max_ctx must be >= 0 (got %lld)", (long long)max_ctx);
+  if (H % Hkv != 0)
+    return fail(FA_EINVAL, "key/value heads (%lld) must divide query heads (%lld)",
+                (long long)Hkv, (long long)H);
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_EINVAL, "unknown dtype %d", dtype);
+  int sh = 0;
+  while (sh < 10 && (int64_t(1) << sh) < block_size) ++sh;
+  if ((int64_t(1) << sh) != block_size)
+    return fail(FA_EUNSUPPORTED, "no decode kernel for block_size=%lld (supported: powers of "
+                "two up to 1024)", (long long)block_size);
+  int64_t cap, bhq, bhqd, tab, t;
+  if (!mul_ok(max_blocks, block_size, &cap) || !mul_ok(B, H, &bhq) || !mul_ok(bhq, n_q, &bhq) ||
+      !mul_ok(bhq, d, &bhqd) || !mul_ok(B, max_blocks, &tab) || !mul_ok(num_blocks, Hkv, &t) ||
+      !mul_ok(t, block_size, &t) || !mul_ok(t, d, &t) || !mul_ok(t, 2, &t))
+    return fail(FA_EINVAL, "tensor size overflows 64-bit byte counts");
+  if (cap > INT32_MAX || tab > INT32_MAX || bhqd > INT32_MAX || num_blocks > INT32_MAX ||
+      n_q > 65536)
+    return fail(FA_EINVAL, "sizes exceed the 32-bit index range of the decode kernels");
+  if (max_ctx < cap) cap = max_ctx;
+  if (dtype == FA_F32 || !fa::decode_plan((int)d, B, H, Hkv, n_q, cap, plan))
+    return fail(FA_EUNSUPPORTED, "no decode kernel for dtype=%s d=%lld (supported: bf16/f16 "
+                "with d in {64,128})", dtype_name(dtype), (long long)d);
+  if (plan->grid > INT32_MAX) return fail(FA_EINVAL, "grid too large");
+  *bs_shift = sh;
+  *ctx_cap = cap;
+  return FA_OK;
+}
+
+fa_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
+                      void *workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                      int64_t Hkv, int64_t n_q, int64_t d, int64_t num_blocks,
+                      int64_t block_size, int64_t max_blocks, int64_t max_ctx, int dtype,
+                      float scale, void *stream) {
+  g_err[0] = '\0';
+  const void *need16[4] = {q, k_cache, v_cache, o};
+  for (int i = 0; i < 4; ++i) {
+    if (!need16[i]) return fail(FA_EINVAL, "null pointer argument (q, k_cache, v_cache or o)");
+    if ((uintptr_t)need16[i] % 16 != 0)
+      return fail(FA_EINVAL, "pointer argument %d is not 16-byte aligned", i);
+  }
+  const void *need4[3] = {block_table, ctx_lens, lse};
+  for (int i = 0; i < 3; ++i) {
+    if (!need4[i]) return fail(FA_EINVAL, "null pointer argument (block_table, ctx_lens or lse)");
+    if ((uintptr_t)need4[i] % 4 != 0)
+      return fail(FA_EINVAL, "block_table, ctx_lens and lse must be 4-byte aligned");
+  }
+  if (!isfinite(scale)) return fail(FA_EINVAL, "scale must be finite");
+  int sh = 0;
+  int64_t cap = 0;
+  fa::DecodePlan plan;
+  fa_status st = decode_sizes(B, H, Hkv, n_q, d, num_blocks, block_size, max_blocks, max_ctx,
+                              dtype, &sh, &cap, &plan);
+  if (st != FA_OK) return st;
+  if (plan.ws_bytes > 0) {
+    if (!workspace || (uintptr_t)workspace % 16 != 0)
+      return fail(FA_EINVAL, "this launch needs a 16-byte-aligned workspace of %lld bytes",
+                  (long long)plan.ws_bytes);
+    if ((int64_t)workspace_bytes < plan.ws_bytes)
+      return fail(FA_EINVAL, "workspace too small: %zu bytes given, %lld needed", workspace_bytes,
+                  (long long)plan.ws_bytes);
+  }
+  const int64_t esz = 2;
+  const int64_t q_bytes = B * H * n_q * d * esz, lse_bytes = B * H * n_q * 4;
+  const int64_t cache_bytes = num_blocks * Hkv * block_size * d * esz;
+  const int64_t table_bytes = B * max_blocks * 4, ctx_bytes = B * 4;
+  const void *ins[5] = {q, k_cache, v_cache, block_table, ctx_lens};
+  const int64_t in_n[5] = {q_bytes, cache_bytes, cache_bytes, table_bytes, ctx_bytes};
+  const void *outs[3] = {o, lse, workspace};
+  const int64_t out_n[3] = {q_bytes, lse_bytes, plan.ws_bytes};
+  static const char *out_names[3] = {"o", "lse", "workspace"};
+  for (int i = 0; i < 3; ++i) {
+    if (out_n[i] == 0) continue;
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], out_n[i], ins[j], in_n[j]))
+        return fail(FA_EINVAL, "%s overlaps an input", out_names[i]);
+    for (int j = i + 1; j < 3; ++j)
+      if (out_n[j] > 0 && overlaps(outs[i], out_n[i], outs[j], out_n[j]))
+        return fail(FA_EINVAL, "%s and %s overlap", out_names[i], out_names[j]);
+  }
+
+  fa::DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.o = o;
+  a.lse = lse;
+  a.ws_o = plan.ws_bytes > 0 ? (float *)workspace : nullptr;
+  a.ws_lse = plan.ws_bytes > 0 ? (float *)workspace + B * H * n_q * plan.n_splits * d : nullptr;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.Hkv = (int)Hkv;
+  a.n_q = (int)n_q;
+  a.num_blocks = (int)num_blocks;
+  a.bs_shift = sh;
+  a.max_blocks = (int)max_blocks;
+  a.ctx_cap = (int)cap;
+  a.split_len = plan.split_len;
+  a.n_splits = plan.n_splits;
+  a.rows = plan.rows;
+  a.row_slices = plan.row_slices;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+
+  fa::LaunchInfo info = {nullptr, 0, 0};
+  hipError_t err = hipSuccess;
+  const fa::DType dt = dtype == FA_BF16 ? fa::kBF16 : fa::kF16;
+  fa::decode_paged(dt, (int)d, &a, &plan, nullptr, false, &info, &err);
+  if (log_enabled())
+    fprintf(stderr, "fa_decode_paged: kernel=%s grid=%lld splits=%d split_len=%d row_slices=%d "
+            "B=%lld H=%lld Hkv=%lld n_q=%lld d=%lld block_size=%lld\n", info.name,
+            (long long)plan.grid, plan.n_splits, plan.split_len, plan.row_slices, (long long)B,
+            (long long)H, (long long)Hkv, (long long)n_q, (long long)d, (long long)block_size);
+  fa::decode_paged(dt, (int)d, &a, &plan, (hipStream_t)stream, true, &info, &err);
+  if (err != hipSuccess)
+    return fail(FA_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +389,32 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
                  int64_t window, float scale, void *stream) {
   return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, S, d, dtype, mask, window,
                   scale, stream);
+}
+
+fa_status fa_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_table, const int32_t *ctx_lens, void *o,
+                          float *lse, void *workspace, size_t workspace_bytes, int64_t B,
+                          int64_t H, int64_t Hkv, int64_t n_q, int64_t d, int64_t num_blocks,
+                          int64_t block_size, int64_t max_blocks, int64_t max_ctx, int dtype,
+                          float scale, void *stream) {
+  return decode_impl(q, k_cache, v_cache, block_table, ctx_lens, o, lse, workspace,
+                     workspace_bytes, B, H, Hkv, n_q, d, num_blocks, block_size, max_blocks,
+                     max_ctx, dtype, scale, stream);
+}
+
+fa_status fa_decode_workspace_size(int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t d,
+                                   int64_t num_blocks, int64_t block_size, int64_t max_blocks,
+                                   int64_t max_ctx, int dtype, size_t *bytes) {
+  g_err[0] = '\0';
+  if (!bytes) return fail(FA_EINVAL, "null pointer argument");
+  int sh = 0;
+  int64_t cap = 0;
+  fa::DecodePlan plan;
+  fa_status st = decode_sizes(B, H, Hkv, n_q, d, num_blocks, block_size, max_blocks, max_ctx,
+                              dtype, &sh, &cap, &plan);
+  if (st != FA_OK) return st;
+  *bytes = (size_t)plan.ws_bytes;
+  return FA_OK;
 }
 
 fa_status fa_query(int64_t d, int dtype, int mask, char *kernel_name, size_t len) {

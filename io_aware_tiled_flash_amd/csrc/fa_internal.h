@@ -36,6 +36,32 @@ struct BwdArgs {
   float scale_log2;        // scale * log2(e)
 };
 
+// Arguments of one paged-cache decode launch, already validated on the host.
+struct DecodeArgs {
+  const void *q;                    // [B, H, n_q, d]
+  const void *k_cache, *v_cache;    // [num_blocks, Hkv, block_size, d]
+  const int32_t *block_table;       // [B, max_blocks]
+  const int32_t *ctx_lens;          // [B]
+  void *o;                          // [B, H, n_q, d]
+  float *lse;                       // [B, H, n_q]
+  float *ws_o;                      // [B*H*n_q, n_splits, d] partial outputs (n_splits > 1)
+  float *ws_lse;                    // [B*H*n_q, n_splits]    partial logsumexps
+  int B, H, Hkv, n_q;
+  int num_blocks, bs_shift, max_blocks;
+  int ctx_cap;                      // min(max_ctx, max_blocks * block_size)
+  int split_len, n_splits;          // tokens per work-group, work-groups per request
+  int rows, row_slices;             // query rows per work-group, work-groups per split
+  float scale_log2;
+};
+
+// How a decode launch is cut up; a pure function of the sizes, shared by the
+// workspace query and the launch.
+struct DecodePlan {
+  int rows, row_slices, split_len, n_splits;
+  int64_t grid;                     // work-groups of the split kernel
+  int64_t ws_bytes;                 // workspace the launch needs (0: none)
+};
+
 // Query head (index into the B*H heads of q, o, lse) and key/value head
 // (index into the B*Hkv heads of k, v) served by work-group slot s in
 // [0, B*H).  Query head h of batch b reads key/value head h / (H / Hkv).
@@ -73,5 +99,13 @@ bool f32_forward(int d, int mask, const FwdArgs *a, hipStream_t stream, bool lau
 // kernel.
 bool mfma_backward(DType dt, int d, int mask, const BwdArgs *a, hipStream_t stream,
                    bool launch, LaunchInfo *info, hipError_t *err);
+// Paged-cache decode: the plan of a launch (false when d has no kernel), and
+// the launch itself (split kernel, then the merge kernel when n_splits > 1).
+bool decode_plan(int d, int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t ctx_cap,
+                 DecodePlan *plan);
+// Split kernel (and, when n_splits > 1, the merge kernel) on `stream`.
+// Returns false when no instance exists for (dtype, d).
+bool decode_paged(DType dt, int d, const DecodeArgs *a, const DecodePlan *plan,
+                  hipStream_t stream, bool launch, LaunchInfo *info, hipError_t *err);
 
 }  // namespace fa

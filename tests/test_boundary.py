@@ -29,8 +29,8 @@ def _declared_functions():
 
 def test_library_builds_and_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == ["fa_abi_version", "fa_bwd", "fa_fwd", "fa_fwd_gqa", "fa_last_error",
-                     "fa_query", "fa_status_str"]
+    assert names == ["fa_abi_version", "fa_bwd", "fa_decode_paged", "fa_decode_workspace_size",
+                     "fa_fwd", "fa_fwd_gqa", "fa_last_error", "fa_query", "fa_status_str"]
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -194,6 +194,85 @@ def test_backward_refuses_host_tensors():
     lse = torch.zeros(1, 1, 8)
     with pytest.raises(fa.FaError) as e:
         fa.backward(q, q, q, q, lse, q, mask="causal")
+    assert e.value.status == fa.FA_EINVAL
+
+
+DEC = dict(q=A, k_cache=A + 16 * MB, v_cache=A + 64 * MB, block_table=A + 112 * MB,
+           ctx_lens=A + 113 * MB, o=A + 114 * MB, lse=A + 115 * MB, workspace=A + 128 * MB,
+           workspace_bytes=64 * MB, B=4, H=8, Hkv=2, n_q=1, d=128, num_blocks=1000,
+           block_size=16, max_blocks=64, max_ctx=1024, dtype=2, scale=0.088, stream=None)
+DEC_ORDER = ["q", "k_cache", "v_cache", "block_table", "ctx_lens", "o", "lse", "workspace",
+             "workspace_bytes", "B", "H", "Hkv", "n_q", "d", "num_blocks", "block_size",
+             "max_blocks", "max_ctx", "dtype", "scale", "stream"]
+
+
+def _call_decode(**kw):
+    # caches [1000, 2, 16, 128] bf16 = 8000 KiB each; q/o [4, 8, 1, 128] = 8 KiB
+    args = dict(DEC)
+    args.update(kw)
+    return fa.fa_decode_paged(*[args[n] for n in DEC_ORDER])
+
+
+def _ws(**kw):
+    args = dict(DEC)
+    args.update(kw)
+    return fa.fa_decode_workspace_size(*[args[n] for n in DEC_ORDER[9:19]])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(q=0), "null"), (dict(block_table=0), "null"), (dict(lse=0), "null"),
+    (dict(k_cache=A + 16 * MB + 8), "aligned"), (dict(ctx_lens=A + 113 * MB + 2), "aligned"),
+    (dict(B=0), "sizes"), (dict(n_q=0), "sizes"), (dict(num_blocks=0), "sizes"),
+    (dict(block_size=0), "sizes"), (dict(max_blocks=0), "sizes"), (dict(max_ctx=-1), "max_ctx"),
+    (dict(Hkv=3), "divide"), (dict(dtype=7), "dtype"), (dict(scale=float("inf")), "finite"),
+    (dict(o=A + 16 * MB + 4096), "o overlaps"),                 # inside k_cache
+    (dict(lse=A + 112 * MB + 64), "lse overlaps"),              # inside block_table
+    (dict(o=A + 115 * MB - 16), "o and lse overlap"),
+    (dict(B=1 << 40, H=1 << 30, Hkv=1 << 30), "overflow"),
+    (dict(max_blocks=1 << 28, block_size=1024), "index range"),
+])
+def test_decode_invalid_arguments_are_rejected_before_any_launch(kw, needle):
+    st = _call_decode(**kw)
+    assert st == fa.FA_EINVAL, (st, fa.fa_last_error())
+    assert needle in fa.fa_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=0), dict(d=96), dict(d=256), dict(block_size=24),
+                                dict(block_size=2048)])
+def test_decode_unsupported_configuration_is_an_error(kw):
+    assert _call_decode(**kw) == fa.FA_EUNSUPPORTED
+    assert "no decode kernel" in fa.fa_last_error()
+
+
+def test_decode_workspace_rules():
+    # many (request, head) pairs and short contexts: no split, no workspace
+    assert _ws(B=256, H=40, Hkv=40, max_ctx=2048, max_blocks=128) == 0
+    # few long requests: split, and the workspace holds a row of d + 1 floats
+    # per (query row, split)
+    need = _ws(B=1, H=8, Hkv=2, max_ctx=1024)
+    assert need > 0 and need % (1 * 8 * 1 * 129 * 4) == 0
+    n_splits = need // (8 * 129 * 4)
+    assert n_splits >= 2
+    assert _ws(B=1, H=8, Hkv=2, max_ctx=2 * 1024, max_blocks=128) >= need
+    # max_ctx beyond what the table can hold changes nothing
+    assert _ws(max_ctx=10 ** 6) == _ws(max_ctx=64 * 16)
+    # a needed workspace that is missing or too small is refused
+    st = _call_decode(B=1, workspace=0)
+    assert st == fa.FA_EINVAL and "workspace" in fa.fa_last_error()
+    st = _call_decode(B=1, workspace_bytes=need - 4)
+    assert st == fa.FA_EINVAL and "too small" in fa.fa_last_error()
+    st = _call_decode(B=1, workspace=A + 16 * MB + 1024, d=96)
+    assert st == fa.FA_EUNSUPPORTED  # size checks come first; nothing launched
+    st = _call_decode(B=1, workspace=A + 16 * MB + 1024)
+    assert st == fa.FA_EINVAL and "workspace overlaps" in fa.fa_last_error()
+
+
+def test_decode_refuses_host_tensors():
+    q = torch.zeros(1, 1, 1, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(2, 1, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FaError) as e:
+        fa.decode(q, kc, kc, torch.zeros(1, 2, dtype=torch.int32),
+                  torch.ones(1, dtype=torch.int32), max_ctx=32)
     assert e.value.status == fa.FA_EINVAL
 
 
