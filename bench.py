@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0
 BWD_FLOP_RATIO = 2.5
 BWD_KERNELS = ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel")
 GRAD_SEED_OFFSET = 7919  # dO is drawn with seed = the workload's seed + this
+DECODE_DEFAULT = "decode_opt13b_b256"
 CSRC = os.path.join(ROOT, "io_aware_tiled_flash_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -125,6 +126,110 @@ def cpu_baseline_bwd(w, q, k, v, do, target_s: float):
             "seconds": round(el, 2)}
 
 
+def cpu_baseline_decode(w, q, kc, vc, table, ctx, target_s: float):
+    """Time the fp64 oracle on whole requests until ~target_s; GB/s of the
+    same byte accounting as the GPU figure, over the requests it finished."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import paged_decode_ref
+    from workloads import kv_bytes_per_token
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    done = []
+    while True:
+        b = len(done)
+        paged_decode_ref(q, kc, vc, table, ctx, max_ctx=w.max_ctx, scale=w.scale, requests=[b])
+        done.append(b)
+        el = time.perf_counter() - t0
+        if el >= target_s or len(done) >= w.B:
+            break
+    c = ctx.numpy()[done]
+    # the same accounting as DecodeWorkload.compulsory_bytes, for these requests
+    byt = int(c.sum()) * kv_bytes_per_token(w.Hkv, w.d, w.esz) + \
+        len(done) * w.H * w.n_q * (2 * w.d * w.esz + 4)
+    return {"value": byt / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} of {w.B} requests of {w.name} (every head and row; fp64 "
+                      f"numpy gather + softmax), {el:.1f} s", "seconds": round(el, 2)}
+
+
+def bench_decode(args) -> int:
+    """One step = one fa_decode_paged call over the whole batch of requests."""
+    import torch
+
+    import io_aware_tiled_flash_amd as fa
+    from workloads import DECODE_WORKLOADS, generate_decode
+
+    name = args.workload if args.workload in DECODE_WORKLOADS else DECODE_DEFAULT
+    w = DECODE_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    host = generate_decode(w)
+    q, kc, vc, table, ctx = (t.to(dev) for t in host)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.n_q), dtype=torch.float32, device=dev)
+    nb, mb = kc.shape[0], table.shape[1]
+    dt = fa.DTYPES[w.dtype]
+    ws_bytes = fa.fa_decode_workspace_size(w.B, w.H, w.Hkv, w.n_q, w.d, nb, w.block_size, mb,
+                                           w.max_ctx, dt)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = (q.data_ptr(), kc.data_ptr(), vc.data_ptr(), table.data_ptr(), ctx.data_ptr(),
+            o.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), w.B, w.H, w.Hkv, w.n_q,
+            w.d, nb, w.block_size, mb, w.max_ctx, dt, float(w.scale), stream.cuda_stream)
+
+    def step():
+        st = fa.fa_decode_paged(*call)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, fa.fa_last_error())
+
+    warm = args.warmup if args.warmup_given else 1000
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    c = host[4].numpy()
+    byt = w.compulsory_bytes(c)
+    gbs = byt / (ms * 1e-3) / 1e9
+    tflops = w.flops(c) / (ms * 1e-3) / 1e12
+    result = {
+        "metric": f"paged decode GB/s on {w.name} (cache rows read once + q, o, lse); "
+                  f"% of HBM peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": warm,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "n_q": w.n_q,
+                   "d": w.d, "block_size": w.block_size, "ctx": [w.ctx_lo, w.ctx_hi],
+                   "cached_tokens": int(c.sum()), "pass": "decode",
+                   "splits": "none" if ws_bytes == 0 else "split + merge",
+                   "kernel": "fa_decode_split_kernel" + ("" if ws_bytes == 0 else
+                                                         " + fa_decode_merge_kernel")},
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "scope": "whole call (one launch without splits, two with)"},
+        "attention_TFLOPs": round(tflops, 2),
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_decode(w, *host, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def copy_calibration(args) -> int:
     """Plain copy of a known byte count per step, for scaling HBM counters."""
     import torch
@@ -151,14 +256,16 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
-                    help="time the forward pass (the headline) or the backward pass")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "decode"), default="fwd",
+                    help="time the forward pass (the headline), the backward pass, or "
+                         "paged-cache decoding (workload default: " + DECODE_DEFAULT + ")")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this "
                          "many MiB per step (reference for HBM byte counters)")
     args = ap.parse_args()
+    args.warmup_given = any(a == "--warmup" or a.startswith("--warmup=") for a in sys.argv[1:])
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -171,12 +278,14 @@ def main() -> int:
     import io_aware_tiled_flash_amd as fa
     from workloads import WORKLOADS, make_grad, make_inputs
 
-    w = WORKLOADS[args.workload]
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
     if args.copy_calibration_mib > 0:
         return copy_calibration(args)
+    if args.pass_ == "decode":
+        return bench_decode(args)
+    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     host = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers, w.kv_heads)
     q, k, v = (t.to(dev) for t in host)
