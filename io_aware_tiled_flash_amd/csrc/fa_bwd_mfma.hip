@@ -139,17 +139,39 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dK and dV: one work-group per 32*NW keys of one key/value head.
+//
+// Software pipeline over the query tiles u of the work-group's stream (one
+// wave, 32 keys; the same for every wave):
+//   phase 1 of step u: S(u) = Q_u K^T and dP(u) = dO_u V^T on the matrix
+//     core, with the vector work of tile u-1 beside them: dS(u-1) =
+//     P(u-1) * (dP(u-1) - D) and its packing;
+//   phase 2 of step u: dV += dO_{u-1}^T P(u-1) and dK += Q_{u-1}^T dS(u-1),
+//     with the weights of tile u beside them: P(u) = exp2(c S(u) - LSE log2 e)
+//     and their packing.
+// Each phase is a fixed sequence of steps (operand read RPD steps ahead, one
+// MFMA, its share of the vector work) separated by scheduling fences, so
+// the matrix core runs while the wave issues the vector work.  Query tiles
+// stream through NST = 4 LDS stages, loaded PF = 2 tiles ahead; the step
+// loop is unrolled over the 4 stage phases so every LDS offset and register
+// buffer choice is a compile-time constant.  Tiles past the end of the
+// stream read out of range (zero fill) and contribute nothing: with Q and
+// dO zero, dP, D and dO^T P all vanish.
 template <class Ty, int D, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BKV = 32 * NW;  // keys per work-group
   constexpr int BQ = 32;        // query rows per streamed tile
   constexpr int NKS = D / 16, NDB = D / 32, KCH = D / 8;
   constexpr int TILE_CHUNKS = BQ * KCH;
+  constexpr int LPW = TILE_CHUNKS / 64 / NW;       // 16-byte loads per wave per tile and tensor
+  constexpr int LOADS = 2 * LPW + 1;               // per wave per tile (Q, dO, one statistic)
+  constexpr int NST = 4, PF = 2, RPD = 3;
+  constexpr int NS1 = 2 * NKS;                     // phase-1 MFMAs (S and dP)
+  constexpr int NS2 = 4 * NDB;                     // phase-2 MFMAs (dV and dK, 2 key halves)
   static_assert(TILE_CHUNKS % (64 * NW) == 0, "tile must split evenly over the waves");
-  __shared__ u32x4 q_lds[2][TILE_CHUNKS];
-  __shared__ u32x4 do_lds[2][TILE_CHUNKS];
-  __shared__ float lse_lds[2][64];
-  __shared__ float dl_lds[2][64];
+  static_assert(NW == 4, "one statistic load per wave: lse, D and two spares");
+  __shared__ u32x4 q_lds[NST][TILE_CHUNKS];
+  __shared__ u32x4 do_lds[NST][TILE_CHUNKS];
+  __shared__ float stat_lds[NST][4][64];           // [stage][lse, D, spare, spare][row]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,7 +181,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int kvi = blockIdx.x % n_kv;  // key/value head (b * Hkv + hk)
   const int kt = blockIdx.x / n_kv;   // key tile; the first ones see the most rows
   const int b = kvi / Hkv, hk = kvi - b * Hkv;
-  const int k0 = kt * BKV, kw0 = k0 + 32 * wave;  // first key of the work-group, of the wave
+  const int k0 = kt * BKV, kw0 = k0 + 32 * wave;
   const float c = a.scale_log2;
 
   const size_t kv_off = (size_t)kvi * (size_t)S * D;
@@ -194,101 +216,223 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dkacc[i] = dvacc[i] = f32x16{};
 
+  // Stream position u -> (query head, first row); past the end: a row
+  // beyond the sequence, whose loads zero-fill.
   auto pair_of = [&](int u, int &bh, int &row0) __attribute__((always_inline)) {
+    if (u >= total) {
+      bh = b * H + hk * group;
+      row0 = S + BQ;
+      return;
+    }
     const int j = u / nq;
     bh = b * H + hk * group + j;
     row0 = (qt_begin + u - j * nq) * BQ;
   };
-  auto issue_loads = [&](int u, int st) __attribute__((always_inline)) {
+  // Direct loads of tile u into stage st; d indexes this wave's LOADS loads.
+  auto dma = [&](int u, int st, int d) __attribute__((always_inline)) {
     int bh, row0;
     pair_of(u, bh, row0);
     const size_t q_off = (size_t)bh * (size_t)S * D;
-    load_rows_tile<D, NW>(rsrc_words((const uint16_t *)a.q + q_off, head_bytes), row0,
-                          q_lds[st], wave, lane);
-    load_rows_tile<D, NW>(rsrc_words((const uint16_t *)a.dout + q_off, head_bytes), row0,
-                          do_lds[st], wave, lane);
-    if (wave == 0)
-      load4_to_lds(rsrc_words(a.lse + (size_t)bh * S, (uint32_t)S * 4u),
-                   (uint32_t)(row0 + lane) * 4u, (uint32_t)(uintptr_t)&lse_lds[st][0]);
-    if (wave == 1)
-      load4_to_lds(rsrc_words(a.delta + (size_t)bh * S, (uint32_t)S * 4u),
-                   (uint32_t)(row0 + lane) * 4u, (uint32_t)(uintptr_t)&dl_lds[st][0]);
+    if (d < 2 * LPW) {
+      const int i = d % LPW;
+      const int blk = wave * LPW + i;
+      const int pos = 64 * blk + lane;
+      const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
+      const uint32_t o = (uint32_t)((row0 + r) * D + 8 * cc) * 2u;
+      if (d < LPW)
+        load16_to_lds(rsrc_words((const uint16_t *)a.q + q_off, head_bytes), o,
+                      (uint32_t)(uintptr_t)&q_lds[st][64 * blk]);
+      else
+        load16_to_lds(rsrc_words((const uint16_t *)a.dout + q_off, head_bytes), o,
+                      (uint32_t)(uintptr_t)&do_lds[st][64 * blk]);
+    } else {
+      const float *src = wave == 1 ? a.delta : a.lse;  // waves 2, 3: spare copies
+      load4_to_lds(rsrc_words(src + (size_t)bh * S, (uint32_t)S * 4u),
+                   (uint32_t)(row0 + lane) * 4u, (uint32_t)(uintptr_t)&stat_lds[st][wave][0]);
+    }
+  };
+
+  // Pipeline registers.  Scores of the current tile; dP of the current and
+  // previous tile (by parity); fp32 weights of the newest tile; packed
+  // weights by parity; packed dS of the previous tile.
+  f32x16 sacc;
+  f32x16 dpacc[2];
+  float pw[16];
+  u32x4 ppk[2][2], dspk[2];
+  dpacc[0] = dpacc[1] = f32x16{};
+
+  // Tile u's rows: row0 + 8*(r/4) + 4*lg + (r%4) for accumulator register r.
+  auto edge_of = [&](int u) __attribute__((always_inline)) {
+    int bh, row0;
+    pair_of(u, bh, row0);
+    if (MASK == kMaskNone) return false;
+    bool e = row0 < kw0 + 31;
+    if (MASK == kMaskWindow) e = e || row0 + BQ - 1 > kw0 - 1 + a.window;
+    return e;
+  };
+  auto fix_mask = [&](int u, u32x4 (&pk)[2]) __attribute__((always_inline)) {
+    int bh, row0;
+    pair_of(u, bh, row0);
+    const int key = kw0 + lq;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = row0 + 8 * (r >> 2) + 4 * lg + (r & 3);
+      bool vis = key <= row;
+      if (MASK == kMaskWindow) vis = vis && key > row - a.window;
+      if (!vis) pw[r] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pk[kk][j] = Ty::pack2(pw[8 * kk + 2 * j], pw[8 * kk + 2 * j + 1]);
+  };
+
+  // One pipeline step u with stage phase P (= u % NST).  HAS_PREV: tile u-1
+  // exists (dS, dV, dK work); HAS_CUR: tile u exists (S, dP, weights).
+  auto step = [&](auto phase_c, auto has_prev_c, auto has_cur_c, int u)
+                  __attribute__((always_inline)) {
+    constexpr int P = decltype(phase_c)::value;
+    constexpr bool HAS_PREV = decltype(has_prev_c)::value, HAS_CUR = decltype(has_cur_c)::value;
+    constexpr int par = P & 1;
+    constexpr int cur = P, prev = (P + NST - 1) % NST, ld = (P + PF) % NST;
+    const char *qc = (const char *)&q_lds[cur][0];
+    const char *dc = (const char *)&do_lds[cur][0];
+    const char *qp = (const char *)&q_lds[prev][0];
+    const char *dp = (const char *)&do_lds[prev][0];
+    // ---- phase 1: S(u), dP(u) | dS(u-1) ----
+    float dl[16];
+    if (HAS_PREV) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 d4 = *(const float4 *)&stat_lds[prev][1][8 * q4 + 4 * lg];
+        dl[4 * q4 + 0] = d4.x;
+        dl[4 * q4 + 1] = d4.y;
+        dl[4 * q4 + 2] = d4.z;
+        dl[4 * q4 + 3] = d4.w;
+      }
+    }
+    u32x4 rop[RPD + 1];
+    auto read_row = [&](int st) __attribute__((always_inline)) {
+      return off.row_op((st & 1) ? dc : qc, st >> 1);
+    };
+    if (HAS_CUR) {
+#pragma unroll
+      for (int st = 0; st < RPD; ++st) rop[st] = read_row(st);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NS1; ++st) {
+      if (HAS_CUR) {
+        if (st + RPD < NS1) rop[(st + RPD) % (RPD + 1)] = read_row(st + RPD);
+        const int ks = st >> 1;
+        if (st & 1)
+          dpacc[par] = Ty::mfma(rop[st % (RPD + 1)], vreg[ks], ks == 0 ? f32x16{} : dpacc[par]);
+        else
+          sacc = Ty::mfma(rop[st % (RPD + 1)], kreg[ks], ks == 0 ? f32x16{} : sacc);
+      }
+      // direct loads of tile u+PF, spread over the phase
+#pragma unroll
+      for (int d = 0; d < LOADS; ++d)
+        if ((d * NS1) / LOADS == st) dma(u + PF, ld, d);
+      if (HAS_PREV) {
+#pragma unroll
+        for (int r = st * 16 / NS1; r < (st + 1) * 16 / NS1; ++r) {
+          const float v = pw[r] * (dpacc[par ^ 1][r] - dl[r]);
+          pw[r] = v;  // pw now holds dS(u-1)
+          if (r & 1) {
+            dspk[r >> 3][(r & 7) >> 1] = Ty::pack2(pw[r - 1], v);
+            pin(dspk[r >> 3][(r & 7) >> 1]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- phase 2: dV, dK of tile u-1 | weights of tile u ----
+    float lv[16];
+    if (HAS_CUR) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 l4 = *(const float4 *)&stat_lds[cur][0][8 * q4 + 4 * lg];
+        lv[4 * q4 + 0] = l4.x * LOG2E;
+        lv[4 * q4 + 1] = l4.y * LOG2E;
+        lv[4 * q4 + 2] = l4.z * LOG2E;
+        lv[4 * q4 + 3] = l4.w * LOG2E;
+      }
+    }
+    // step st: key half kk = st / (2*NDB), d block db = (st / 2) % NDB,
+    // dV (even st) or dK (odd st)
+    u32x4 top[RPD + 1];
+    auto read_tr = [&](int st) __attribute__((always_inline)) {
+      const int kk = st / (2 * NDB), db = (st >> 1) % NDB;
+      return off.tr_op((st & 1) ? qp : dp, kk, db);
+    };
+    if (HAS_PREV) {
+#pragma unroll
+      for (int st = 0; st < RPD; ++st) top[st] = read_tr(st);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NS2; ++st) {
+      if (HAS_PREV) {
+        if (st + RPD < NS2) top[(st + RPD) % (RPD + 1)] = read_tr(st + RPD);
+        const int kk = st / (2 * NDB), db = (st >> 1) % NDB;
+        // the gradient accumulators live in AGPRs: only MFMAs touch them
+        if (st & 1) {
+          dkacc[db] = Ty::mfma(top[st % (RPD + 1)], dspk[kk], dkacc[db]);
+          asm volatile("" : "+a"(dkacc[db]));
+        } else {
+          dvacc[db] = Ty::mfma(top[st % (RPD + 1)], ppk[par ^ 1][kk], dvacc[db]);
+          asm volatile("" : "+a"(dvacc[db]));
+        }
+      }
+      if (HAS_CUR) {
+#pragma unroll
+        for (int r = st * 16 / NS2; r < (st + 1) * 16 / NS2; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lv[r]));
+          pw[r] = p;
+          if (r & 1) {
+            ppk[par][r >> 3][(r & 7) >> 1] = Ty::pack2(pw[r - 1], p);
+            pin(ppk[par][r >> 3][(r & 7) >> 1]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (HAS_CUR && MASK != kMaskNone) {
+      if (edge_of(u)) fix_mask(u, ppk[par]);
+    }
+    // Tile u+1 has landed once only tile u+PF's loads are outstanding.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (PF - 1)) : "memory");
+    __builtin_amdgcn_s_barrier();
   };
 
   // Settle the bookkeeping of the kernel-argument scalar loads before the
-  // loop (see the forward kernel): otherwise every load statement in it
-  // waits for lgkmcnt(0).
+  // loop (see the forward kernel).
   asm volatile("" ::"s"(a.q), "s"(a.dout), "s"(a.lse), "s"(a.delta));
-  if (total > 0) issue_loads(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-
-  for (int u = 0; u < total; ++u) {
-    const int st = u & 1;
-    if (u + 1 < total) issue_loads(u + 1, st ^ 1);
-    int bh, row0;
-    pair_of(u, bh, row0);
-    (void)bh;
-    // Rows of this tile that see none of this wave's keys: skip the math.
-    bool any_visible = row0 < S;
-    if (MASK != kMaskNone) any_visible = any_visible && row0 + BQ - 1 >= kw0;
-    if (MASK == kMaskWindow) any_visible = any_visible && row0 <= kw0 + 31 + a.window - 1;
-    if (any_visible) {
-      const char *qt = (const char *)&q_lds[st][0];
-      const char *dot = (const char *)&do_lds[st][0];
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using T = std::true_type;
+  using F = std::false_type;
+  if (total > 0) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        sacc = Ty::mfma(off.row_op(qt, ks), kreg[ks], sacc);
-        dpacc = Ty::mfma(off.row_op(dot, ks), vreg[ks], dpacc);
-      }
-      // S accumulator: lane (key kw0 + lq), register r -> row
-      // row0 + 8*(r/4) + 4*lg + (r%4).
-      const bool edge = MASK != kMaskNone ? (row0 < kw0 + 31 || (MASK == kMaskWindow &&
-                                                               row0 + BQ - 1 > kw0 - 1 + a.window))
-                                          : false;
-      const bool tail = row0 + BQ > S || kw0 + 31 >= S;
-      float p[16], ds[16];
+    for (int u = 0; u < PF; ++u)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 l4 = *(const float4 *)&lse_lds[st][8 * q4 + 4 * lg];
-        const float4 d4 = *(const float4 *)&dl_lds[st][8 * q4 + 4 * lg];
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * q4 + i;
-          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lv[i] * LOG2E));
-          if (edge || tail) {
-            const int row = row0 + 8 * q4 + 4 * lg + i, key = kw0 + lq;
-            bool vis = row < S && key < S;
-            if (MASK == kMaskCausal) vis = vis && key <= row;
-            if (MASK == kMaskWindow) vis = vis && key <= row && key > row - a.window;
-            if (!vis) pr = 0.f;
-          }
-          p[r] = pr;
-          ds[r] = pr * (dpacc[r] - dv[i]);
-        }
-      }
-      u32x4 ppk[2], dspk[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          ppk[kk][j] = Ty::pack2(p[8 * kk + 2 * j], p[8 * kk + 2 * j + 1]);
-          dspk[kk][j] = Ty::pack2(ds[8 * kk + 2 * j], ds[8 * kk + 2 * j + 1]);
-        }
-      // dV^T += dO^T P and dK^T += Q^T dS (the transposed tile reads give
-      // rows 16*kk + 8*i2 + 4*lg + 0..3, the order of the packed operands).
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dvacc[db] = Ty::mfma(off.tr_op(dot, kk, db), ppk[kk], dvacc[db]);
-          dkacc[db] = Ty::mfma(off.tr_op(qt, kk, db), dspk[kk], dkacc[db]);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      for (int d = 0; d < LOADS; ++d) dma(u, u, d);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (PF - 1)) : "memory");
     __builtin_amdgcn_s_barrier();
+    step(I0{}, F{}, T{}, 0);
+    // steps 1 .. n_main (a multiple of NST, padded with empty tiles), then
+    // the last step, which only finishes tile n_main
+    const int n_main = (total - 1 + NST - 1) / NST * NST;
+    for (int u = 1; u <= n_main; u += NST) {
+      step(I1{}, T{}, T{}, u);
+      step(I2{}, T{}, T{}, u + 1);
+      step(I3{}, T{}, T{}, u + 2);
+      step(I0{}, T{}, T{}, u + 3);
+    }
+    step(I1{}, T{}, F{}, n_main + 1);
   }
 
   // dK = scale * dS^T Q; each lane holds d values of key kw0 + lq.
