@@ -445,15 +445,30 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ: one work-group per 32*NW query rows of one query head.
+//
+// The same software pipeline as the dK/dV kernel, over the key tiles t the
+// work-group visits (each wave: its 32 rows against the tile's 32 keys):
+//   phase 1 of step t: S^T(t) = K_t Q^T and dP^T(t) = V_t dO^T on the matrix
+//     core, with dS^T(t-1) = P(t-1) * (dP^T(t-1) - D) and its packing beside;
+//   phase 2 of step t: dQ^T += K_{t-1}^T dS^T(t-1), with the weights of tile
+//     t, P = exp2(c S^T(t) - LSE log2 e), beside.
+// Keys past the sequence read as zero rows: their dS^T column is multiplied
+// by a zero K row, so they need no mask; causal and window edges get a
+// fix-up on the tiles that straddle them.
 template <class Ty, int D, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int BR = 32 * NW;  // query rows per work-group
   constexpr int BC = 32;       // keys per streamed tile
   constexpr int NKS = D / 16, NDB = D / 32, KCH = D / 8;
   constexpr int TILE_CHUNKS = BC * KCH;
+  constexpr int LPW = TILE_CHUNKS / 64 / NW;
+  constexpr int LOADS = 2 * LPW;                   // K and V, per wave per tile
+  constexpr int NST = 4, PF = 2, RPD = 3;
+  constexpr int NS1 = 2 * NKS;                     // S^T and dP^T MFMAs
+  constexpr int NS2 = 2 * NDB;                     // dQ^T MFMAs (2 key halves)
   static_assert(TILE_CHUNKS % (64 * NW) == 0, "tile must split evenly over the waves");
-  __shared__ u32x4 k_lds[2][TILE_CHUNKS];
-  __shared__ u32x4 v_lds[2][TILE_CHUNKS];
+  __shared__ u32x4 k_lds[NST][TILE_CHUNKS];
+  __shared__ u32x4 v_lds[NST][TILE_CHUNKS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -494,74 +509,153 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
     kt_end = (min(q0 + BR, S) - 1) / BC + 1;
     if (MASK == kMaskWindow) kt_begin = max(0, q0 - a.window + 1) / BC;
   }
+  const int total = kt_end - kt_begin;
 
   const TileOffsets<D> off(lane);
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
 
-  auto issue_loads = [&](int kt, int st) __attribute__((always_inline)) {
-    load_rows_tile<D, NW>(rk, kt * BC, k_lds[st], wave, lane);
-    load_rows_tile<D, NW>(rv, kt * BC, v_lds[st], wave, lane);
+  // Direct loads of stream tile u (key tile kt_begin + u; past the end an
+  // out-of-range tile, zero-filled) into stage st.
+  auto dma = [&](int u, int st, int d) __attribute__((always_inline)) {
+    const int kt = u < total ? kt_begin + u : ntk + 1;
+    const int i = d % LPW;
+    const int blk = wave * LPW + i;
+    const int pos = 64 * blk + lane;
+    const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
+    const uint32_t o = (uint32_t)((kt * BC + r) * D + 8 * cc) * 2u;
+    if (d < LPW)
+      load16_to_lds(rk, o, (uint32_t)(uintptr_t)&k_lds[st][64 * blk]);
+    else
+      load16_to_lds(rv, o, (uint32_t)(uintptr_t)&v_lds[st][64 * blk]);
+  };
+
+  f32x16 sacc, dpacc[2];
+  float pw[16];
+  u32x4 dspk[2];
+  dpacc[0] = dpacc[1] = f32x16{};
+
+  // S^T accumulator register r of tile u holds key k0 + 8*(r/4) + 4*lg + (r%4).
+  auto edge_of = [&](int u) __attribute__((always_inline)) {
+    const int k0 = (kt_begin + u) * BC;
+    if (MASK == kMaskCausal) return k0 + BC - 1 > wr0;
+    if (MASK == kMaskWindow) return k0 + BC - 1 > wr0 || k0 <= wr1 - a.window;
+    return false;
+  };
+  auto fix_mask = [&](int u) __attribute__((always_inline)) {
+    const int k0 = (kt_begin + u) * BC;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * lg + (r & 3);
+      bool vis = key <= row;
+      if (MASK == kMaskWindow) vis = vis && key > row - a.window;
+      if (!vis) pw[r] = 0.f;
+    }
+  };
+
+  auto step = [&](auto phase_c, auto has_prev_c, auto has_cur_c, int u)
+                  __attribute__((always_inline)) {
+    constexpr int P = decltype(phase_c)::value;
+    constexpr bool HAS_PREV = decltype(has_prev_c)::value, HAS_CUR = decltype(has_cur_c)::value;
+    constexpr int par = P & 1;
+    constexpr int cur = P, prev = (P + NST - 1) % NST, ld = (P + PF) % NST;
+    const char *kc = (const char *)&k_lds[cur][0];
+    const char *vc = (const char *)&v_lds[cur][0];
+    const char *kp = (const char *)&k_lds[prev][0];
+    // ---- phase 1: S^T(u), dP^T(u) | dS^T(u-1) ----
+    u32x4 rop[RPD + 1];
+    auto read_row = [&](int st) __attribute__((always_inline)) {
+      return off.row_op((st & 1) ? vc : kc, st >> 1);
+    };
+    if (HAS_CUR) {
+#pragma unroll
+      for (int st = 0; st < RPD; ++st) rop[st] = read_row(st);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NS1; ++st) {
+      if (HAS_CUR) {
+        if (st + RPD < NS1) rop[(st + RPD) % (RPD + 1)] = read_row(st + RPD);
+        const int ks = st >> 1;
+        if (st & 1)
+          dpacc[par] = Ty::mfma(rop[st % (RPD + 1)], doreg[ks], ks == 0 ? f32x16{} : dpacc[par]);
+        else
+          sacc = Ty::mfma(rop[st % (RPD + 1)], qreg[ks], ks == 0 ? f32x16{} : sacc);
+      }
+#pragma unroll
+      for (int d = 0; d < LOADS; ++d)
+        if ((d * NS1) / LOADS == st) dma(u + PF, ld, d);
+      if (HAS_PREV) {
+#pragma unroll
+        for (int r = st * 16 / NS1; r < (st + 1) * 16 / NS1; ++r) {
+          const float v = pw[r] * (dpacc[par ^ 1][r] - drow);
+          pw[r] = v;  // pw now holds dS^T(u-1)
+          if (r & 1) {
+            dspk[r >> 3][(r & 7) >> 1] = Ty::pack2(pw[r - 1], v);
+            pin(dspk[r >> 3][(r & 7) >> 1]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- phase 2: dQ^T of tile u-1 | weights of tile u ----
+    u32x4 top[RPD + 1];
+    auto read_tr = [&](int st) __attribute__((always_inline)) {
+      return off.tr_op(kp, st / NDB, st % NDB);
+    };
+    if (HAS_PREV) {
+#pragma unroll
+      for (int st = 0; st < RPD && st < NS2; ++st) top[st] = read_tr(st);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NS2; ++st) {
+      if (HAS_PREV) {
+        if (st + RPD < NS2) top[(st + RPD) % (RPD + 1)] = read_tr(st + RPD);
+        const int kk = st / NDB, db = st % NDB;
+        dqacc[db] = Ty::mfma(top[st % (RPD + 1)], dspk[kk], dqacc[db]);
+        asm volatile("" : "+a"(dqacc[db]));
+      }
+      if (HAS_CUR) {
+#pragma unroll
+        for (int r = st * 16 / NS2; r < (st + 1) * 16 / NS2; ++r) {
+          pw[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lse2));
+          pin(pw[r]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (HAS_CUR && MASK != kMaskNone) {
+      if (edge_of(u)) fix_mask(u);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (PF - 1)) : "memory");
+    __builtin_amdgcn_s_barrier();
   };
 
   asm volatile("" ::"s"(rk), "s"(rv), "s"(a.dq));
-  if (kt_begin < kt_end) issue_loads(kt_begin, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int st = (kt - kt_begin) & 1;
-    if (kt + 1 < kt_end) issue_loads(kt + 1, st ^ 1);
-    const int k0 = kt * BC;
-    bool any_visible = wr0 < S;
-    if (MASK != kMaskNone) any_visible = any_visible && k0 <= wr1;
-    if (MASK == kMaskWindow) any_visible = any_visible && k0 + BC - 1 > wr0 - a.window;
-    if (any_visible) {
-      const char *kl = (const char *)&k_lds[st][0];
-      const char *vl = (const char *)&v_lds[st][0];
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using T = std::true_type;
+  using F = std::false_type;
+  if (total > 0) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        sacc = Ty::mfma(off.row_op(kl, ks), qreg[ks], sacc);
-        dpacc = Ty::mfma(off.row_op(vl, ks), doreg[ks], dpacc);
-      }
-      // S^T accumulator: lane (row wr0 + lq), register r -> key
-      // k0 + 8*(r/4) + 4*lg + (r%4).
-      bool edge;
-      if (MASK == kMaskNone)
-        edge = k0 + BC > S;
-      else if (MASK == kMaskCausal)
-        edge = k0 + BC - 1 > wr0;
-      else
-        edge = k0 + BC - 1 > wr0 || k0 <= wr1 - a.window;
-      float ds[16];
+    for (int u = 0; u < PF; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lse2));
-        if (edge) {
-          const int key = k0 + 8 * (r >> 2) + 4 * lg + (r & 3);
-          bool vis = key < S;
-          if (MASK == kMaskCausal) vis = key <= row;
-          if (MASK == kMaskWindow) vis = key <= row && key > row - a.window;
-          if (!vis) pr = 0.f;
-        }
-        ds[r] = pr * (dpacc[r] - drow);
-      }
-      u32x4 dspk[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dspk[kk][j] = Ty::pack2(ds[8 * kk + 2 * j], ds[8 * kk + 2 * j + 1]);
-      // dQ^T += K^T dS^T.
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dqacc[db] = Ty::mfma(off.tr_op(kl, kk, db), dspk[kk], dqacc[db]);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      for (int d = 0; d < LOADS; ++d) dma(u, u, d);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (PF - 1)) : "memory");
     __builtin_amdgcn_s_barrier();
+    step(I0{}, F{}, T{}, 0);
+    const int n_main = (total - 1 + NST - 1) / NST * NST;
+    for (int u = 1; u <= n_main; u += NST) {
+      step(I1{}, T{}, T{}, u);
+      step(I2{}, T{}, T{}, u + 1);
+      step(I3{}, T{}, T{}, u + 2);
+      step(I0{}, T{}, T{}, u + 3);
+    }
+    step(I1{}, T{}, F{}, n_main + 1);
   }
 
   if (row < S)
