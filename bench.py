@@ -43,12 +43,16 @@ CSRC = os.path.join(ROOT, "io_aware_tiled_flash_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+# The sources the forward matrix-core kernel is compiled from: a committed
+# counter summary is only used while these are unchanged.
+FWD_SOURCES = ("fa_fwd_mfma.hip", "fa_gfx950.h", "fa_internal.h")
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in FWD_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
