@@ -25,7 +25,7 @@
 //     and the groups, waves and finally the splits are merged with the
 //     logsumexp algebra: O = sum_s exp(LSE_s - LSE) O_s, LSE = log sum_s
 //     exp(LSE_s).
-#include "fa_gfx950.h"
+#include "fa_tile_ops.h"
 
 #include <math.h>
 #include <stdio.h>
@@ -39,6 +39,14 @@ constexpr int kThreads = 256;
 constexpr int kMaxSplitLen = 4096;               // tokens per work-group at most
 constexpr int kMaxTable = kMaxSplitLen + 2;      // table entries one split can touch
 constexpr float kTau = 8.f;                      // lazy-rescale threshold (base 2)
+#ifndef FA_DEC_MFMA_ROWS
+#define FA_DEC_MFMA_ROWS 12
+#endif
+constexpr int kMfmaRows = FA_DEC_MFMA_ROWS;      // query rows per key/value head for MFMA
+#ifndef FA_DEC_MFMA_GROUPS
+#define FA_DEC_MFMA_GROUPS 1024
+#endif
+constexpr int kMfmaGroups = FA_DEC_MFMA_GROUPS;  // work-groups the MFMA path aims for
 
 template <class Ty> struct Dot;
 template <> struct Dot<TBF16> {
@@ -145,17 +153,15 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeArgs a)
   const size_t blk_stride = (size_t)a.Hkv << sh;  // rows per physical block (all heads)
   const uint16_t *kc = (const uint16_t *)a.k_cache + ((size_t)g << sh) * D + 8 * c;
   const uint16_t *vc = (const uint16_t *)a.v_cache + ((size_t)g << sh) * D + 8 * c;
+  // Every lane loads (a token that does not exist reads block 0's first row,
+  // always valid memory; loads under a branch would make the compiler wait
+  // for all of them at the next use); such tokens get weight 0 and a zero V.
   auto fetch = [&](int t, u32x4 &kk, u32x4 &vv) __attribute__((always_inline)) {
     int blk = -1;
     if (t < t1) blk = tab[(t >> sh) - first];
-    if (blk >= 0) {
-      const size_t row = (size_t)blk * blk_stride + (size_t)(t & bs_mask);
-      kk = __builtin_nontemporal_load((const u32x4 *)(kc + row * D));
-      vv = __builtin_nontemporal_load((const u32x4 *)(vc + row * D));
-    } else {
-      kk = u32x4{0, 0, 0, 0};
-      vv = u32x4{0, 0, 0, 0};
-    }
+    const size_t row = blk >= 0 ? (size_t)blk * blk_stride + (size_t)(t & bs_mask) : 0;
+    kk = __builtin_nontemporal_load((const u32x4 *)(kc + row * D));
+    vv = __builtin_nontemporal_load((const u32x4 *)(vc + row * D));
     return blk >= 0;
   };
 
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeArgs a)
     float vf[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x2 x = Ty::unpack2(vv[j]);
+      const f32x2 x = Ty::unpack2(ok ? vv[j] : 0u);
       vf[2 * j] = x[0];
       vf[2 * j + 1] = x[1];
     }
@@ -293,6 +299,297 @@ __global__ __launch_bounds__(kThreads) void fa_decode_merge_kernel(DecodeArgs a)
   if (lane == 0) a.lse[row] = lse;
 }
 
+// Matrix-core variant, used when a key/value head serves many query rows
+// (grouped heads and several new tokens): 32 rows per work-group, padded.  It is
+// the forward kernel's decomposition with the keys gathered through the
+// block table: per wave and step, 32 keys; S^T = K Q^T with K loaded from the
+// cache straight into MFMA operand registers (lane: one key, 16 bytes of its
+// row), the running softmax over the 16 keys a lane holds for its row (and
+// the other 16 in the partner lane), and O^T += V^T P^T with V^T read by
+// ds_read_b64_tr_b16 from a wave-private LDS tile the wave fills from
+// registers.  The next step's rows are loaded while the current one computes.
+// Waves take every fourth step of the split and are merged through LDS at
+// the end, then the splits as in the vector kernel.
+template <class Ty, int D>
+__global__ __launch_bounds__(kThreads, 1) void fa_decode_mfma_kernel(DecodeArgs a) {
+  constexpr int NKS = D / 16, NDB = D / 32, KCH = D / 8;
+  constexpr int TK = 32;                           // keys per wave step
+  constexpr int VT_BYTES = TK * D * 2;             // one wave's V tile
+  static_assert(2 * TK * D * 4 <= 4 * VT_BYTES, "merge buffer must fit in the V tiles");
+  __shared__ int tab[kMaxTable];
+  __shared__ __attribute__((aligned(16))) char vt_raw[4 * VT_BYTES];
+  __shared__ float mrg_m[2][TK], mrg_l[2][TK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, lg = lane >> 5;
+
+  const int pairs = a.B * a.Hkv;
+  int rs = 0, base = blockIdx.x;
+  if (a.row_slices > 1) {
+    const int per = 8 * a.row_slices;
+    const int grp = base / per, rem = base - grp * per;
+    rs = rem >> 3;
+    base = grp * 8 + (rem & 7);
+  }
+  if (base >= pairs * a.n_splits) return;
+  const int pair = base % pairs, split = base / pairs;
+  const int b = pair / a.Hkv, g = pair - b * a.Hkv;
+  const int n = min(max(a.ctx_lens[b], 0), a.ctx_cap);
+  const int ns_b = max(1, (n + a.split_len - 1) / a.split_len);
+  if (split >= ns_b) return;
+  const int t0 = split * a.split_len, t1 = min(n, t0 + a.split_len);
+  const int group = a.H / a.Hkv, rows_total = group * a.n_q;
+  const int sh = a.bs_shift, bs_mask = (1 << sh) - 1;
+
+  const int first = t0 >> sh;
+  const int cnt = t1 > t0 ? ((t1 - 1) >> sh) - first + 1 : 0;
+  for (int e = tid; e < cnt; e += kThreads) {
+    const int v = a.block_table[(size_t)b * a.max_blocks + first + e];
+    tab[e] = (v >= 0 && v < a.num_blocks) ? v : -1;
+  }
+
+  // This lane's query row (lanes lq and lq + 32 share it).
+  const int rho = rs * TK + lq;
+  const bool row_ok = rho < rows_total;
+  int out_row = 0, pos = -1;
+  if (row_ok) {
+    const int j = rho / a.n_q, i = rho - j * a.n_q;
+    out_row = (b * a.H + g * group + j) * a.n_q + i;
+    pos = n - a.n_q + i;
+  }
+  u32x4 qreg[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qreg[ks] = row_ok ? *(const u32x4 *)((const uint16_t *)a.q + (size_t)out_row * D + 16 * ks +
+                                         8 * lg)
+                      : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qreg[ks]));
+  const int min_pos = n - a.n_q;  // smallest query position of the request
+  __syncthreads();
+
+  const size_t blk_stride = (size_t)a.Hkv << sh;
+  const uint16_t *kc = (const uint16_t *)a.k_cache + ((size_t)g << sh) * D;
+  const uint16_t *vc = (const uint16_t *)a.v_cache + ((size_t)g << sh) * D;
+  char *vt = vt_raw + wave * VT_BYTES;
+  const TileOffsets<D> off(lane);
+
+  // Rows of step j's key lq: K operand chunks 2*ks + lg, V chunks 2*ks + lg.
+  // Every lane loads (a key that does not exist reads block 0's first row,
+  // always valid memory): loads under a branch would make the compiler wait
+  // for all of them before the next use of any.  Such keys are masked from
+  // the scores and their V rows are zeroed before use.
+  struct Rows {
+    u32x4 k[NKS], v[NKS];
+  };
+  auto fetch = [&](int j) __attribute__((always_inline)) {
+    const int key = t0 + TK * j + lq;
+    int blk = -1;
+    if (key < t1) blk = tab[(key >> sh) - first];
+    const size_t row = blk >= 0
+                           ? ((size_t)blk * blk_stride + (size_t)(key & bs_mask)) * D + 8 * lg
+                           : (size_t)(8 * lg);
+    Rows out;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      out.k[ks] = __builtin_nontemporal_load((const u32x4 *)(kc + row + 16 * ks));
+      out.v[ks] = __builtin_nontemporal_load((const u32x4 *)(vc + row + 16 * ks));
+    }
+    return out;
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  const float cl2 = a.scale_log2;
+  const int n_steps = (t1 - t0 + TK - 1) / TK;
+
+  auto body = [&](int j, const Rows &cur) __attribute__((always_inline)) {
+    // Keys of this step that exist (valid block, inside the split).
+    const int tk = t0 + TK * j;
+    bool key_ok;
+    {
+      const int key = tk + lq;
+      key_ok = key < t1;
+      if (key_ok) key_ok = tab[(key >> sh) - first] >= 0;
+    }
+    const int kvalid = (int)(uint32_t)__builtin_amdgcn_ballot_w64(key_ok);  // bit k: key k
+    // V rows of step j into the wave's tile (row lq, chunk 2*ks + lg); rows of
+    // keys that do not exist are zero.
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 v = cur.v[ks];
+      if (kvalid != -1) v = key_ok ? v : u32x4{0, 0, 0, 0};
+      *(u32x4 *)(vt + lq * (D * 2) + 16 * swz<D>(lq, 2 * ks + lg)) = v;
+    }
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) sacc = Ty::mfma(cur.k[ks], qreg[ks], sacc);
+    float sv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = sacc[r] * cl2;
+    if (kvalid != -1 || tk + TK - 1 > min_pos) {  // some key hidden from some row
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + 4 * lg + (r & 3);
+        const bool vis = ((kvalid >> kr) & 1) && tk + kr <= pos;
+        if (!vis) sv[r] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+    for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sv[r]), r + 1 < 16 ? sv[r + 1] : sv[r]);
+    mx = fmaxf(mx, wave_partner(mx));
+    const float m_new = mx > m + kTau ? mx : m;
+    if (__builtin_amdgcn_ballot_w64(m_new != m) != 0) {  // rare: move the offsets
+      const float al = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= al;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= al;
+      m = m_new;
+    }
+    const float mu = m == -INFINITY ? 0.f : m;
+    float pw[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pw[r] = __builtin_amdgcn_exp2f(sv[r] - mu);
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ls += pw[r];
+    l += ls;
+    u32x4 ppk[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        ppk[kk][jj] = Ty::pack2(pw[8 * kk + 2 * jj], pw[8 * kk + 2 * jj + 1]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = Ty::mfma(off.tr_op(vt, kk, db), ppk[kk], oacc[db]);
+  };
+
+  // Two register sets alternate (no copy between them: copying a loaded
+  // value would wait for its load), so one step's rows are always in flight
+  // while the other step computes.
+  Rows ra = fetch(wave);
+  for (int j = wave; j < n_steps; j += 8) {
+    const Rows rb = fetch(j + 4);
+    body(j, ra);
+    ra = fetch(j + 8);
+    if (j + 4 < n_steps) body(j + 4, rb);
+  }
+
+  // Merge the four waves: 2 and 3 into 0 and 1, then 1 into 0.
+  const float lrow = l + wave_partner(l);
+  float *mo = (float *)vt_raw;  // [2][TK rows][D] fp32, over the V tiles
+  __syncthreads();
+  auto put = [&](int slot) __attribute__((always_inline)) {
+    if (lg == 0) {
+      mrg_m[slot][lq] = m;
+      mrg_l[slot][lq] = lrow;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(float4 *)&mo[(slot * TK + lq) * D + 32 * db + 8 * q4 + 4 * lg] =
+            float4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2],
+                   oacc[db][4 * q4 + 3]};
+  };
+  float lr = lrow;
+  auto take = [&](int slot) __attribute__((always_inline)) {
+    const float m2 = mrg_m[slot][lq], l2 = mrg_l[slot][lq];
+    const float mm = fmaxf(m, m2);
+    const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+    const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+    lr = a1 * lr + a2 * l2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v = *(const float4 *)&mo[(slot * TK + lq) * D + 32 * db + 8 * q4 + 4 * lg];
+        oacc[db][4 * q4 + 0] = a1 * oacc[db][4 * q4 + 0] + a2 * v.x;
+        oacc[db][4 * q4 + 1] = a1 * oacc[db][4 * q4 + 1] + a2 * v.y;
+        oacc[db][4 * q4 + 2] = a1 * oacc[db][4 * q4 + 2] + a2 * v.z;
+        oacc[db][4 * q4 + 3] = a1 * oacc[db][4 * q4 + 3] + a2 * v.w;
+      }
+    m = mm;
+  };
+  if (wave >= 2) put(wave - 2);
+  __syncthreads();
+  if (wave < 2) take(wave);
+  __syncthreads();
+  if (wave == 1) {
+    if (lg == 0) {
+      mrg_m[0][lq] = m;
+      mrg_l[0][lq] = lr;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(float4 *)&mo[lq * D + 32 * db + 8 * q4 + 4 * lg] =
+            float4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2],
+                   oacc[db][4 * q4 + 3]};
+  }
+  __syncthreads();
+  if (wave != 0 || !row_ok) return;
+  take(0);
+
+  const bool empty = !(lr > 0.f);
+  const float inv = empty ? 0.f : 1.f / lr;
+  const float lv = empty ? -INFINITY : (m + __builtin_amdgcn_logf(lr)) * 0.69314718055994531f;
+  if (ns_b == 1) {
+    uint16_t *orow = (uint16_t *)a.o + (size_t)out_row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x2 w;
+        w[0] = Ty::pack2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv);
+        w[1] = Ty::pack2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+        *(u32x2 *)(orow + 32 * db + 8 * q4 + 4 * lg) = w;
+      }
+    if (lg == 0) a.lse[out_row] = lv;
+  } else {
+    const size_t slot = (size_t)out_row * a.n_splits + split;
+    float *wo = a.ws_o + slot * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(float4 *)&wo[32 * db + 8 * q4 + 4 * lg] =
+            float4{oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv,
+                   oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv};
+    if (lg == 0) a.ws_lse[slot] = lv;
+  }
+}
+
+template <class Ty, int D>
+bool run_decode_mfma(const DecodeArgs *a, const DecodePlan *p, hipStream_t stream, bool launch,
+                     LaunchInfo *info, hipError_t *err) {
+  static char name[96];
+  snprintf(name, sizeof(name), "fa_decode_paged_mfma<%s,d%d,rows32>", Ty::kName, D);
+  info->name = name;
+  info->block_rows = 32;
+  info->threads = kThreads;
+  if (!launch) return true;
+  DecodeArgs args = *a;
+  void *kargs[] = {&args};
+  *err = hipLaunchKernel((const void *)&fa_decode_mfma_kernel<Ty, D>, dim3((unsigned)p->grid),
+                         dim3(kThreads), kargs, 0, stream);
+  if (*err != hipSuccess || p->n_splits == 1) return true;
+  const int64_t rows = (int64_t)a->B * a->H * a->n_q;
+  *err = hipLaunchKernel((const void *)&fa_decode_merge_kernel<Ty, D>,
+                         dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), kargs, 0, stream);
+  return true;
+}
+
 template <class Ty, int D, int R>
 bool run_decode(const DecodeArgs *a, const DecodePlan *p, hipStream_t stream, bool launch,
                 LaunchInfo *info, hipError_t *err) {
@@ -320,7 +617,7 @@ bool decode_by_rows(const DecodeArgs *a, const DecodePlan *p, hipStream_t s, boo
     case 1: return run_decode<Ty, D, 1>(a, p, s, launch, info, err);
     case 2: return run_decode<Ty, D, 2>(a, p, s, launch, info, err);
     case 4: return run_decode<Ty, D, 4>(a, p, s, launch, info, err);
-    case 8: return run_decode<Ty, D, 8>(a, p, s, launch, info, err);
+    case 32: return run_decode_mfma<Ty, D>(a, p, s, launch, info, err);
   }
   return false;
 }
@@ -341,12 +638,22 @@ bool decode_plan(int d, int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t 
                  DecodePlan *p) {
   if (d != 64 && d != 128) return false;
   const int64_t rows_total = (H / Hkv) * n_q;
-  p->rows = rows_total <= 1 ? 1 : rows_total <= 2 ? 2 : rows_total <= 4 ? 4 : 8;
+  // A key/value head serving many query rows goes to the matrix-core kernel
+  // (32 rows per work-group); up to kMfmaRows - 1 rows stay on the vector
+  // ALUs, which measured faster there.  The vector kernel takes at most 4
+  // rows per work-group: more rows slices (whose repeated cache reads hit
+  // the shared L2) measured faster than 8-row work-groups, whose registers
+  // cut the waves per SIMD from 5 to 3.
+  p->rows = rows_total <= 1 ? 1 : rows_total <= 2 ? 2 : rows_total < kMfmaRows ? 4 : 32;
   p->row_slices = (int)((rows_total + p->rows - 1) / p->rows);
   // Enough work-groups to fill the chip several times over: split each
   // context when requests x key/value heads x row slices alone are too few.
+  // The vector kernel runs several work-groups per CU and wants many short
+  // ones; the matrix-core kernel runs one per CU and wants fewer, longer
+  // ones (its per-work-group setup and merge are dearer).
   const int64_t units = B * Hkv * p->row_slices;
-  const int64_t want = units >= 2048 ? 1 : (2048 + units - 1) / units;
+  const int64_t target = p->rows == 32 ? kMfmaGroups : 2048;
+  const int64_t want = units >= target ? 1 : (target + units - 1) / units;
   int64_t len = (ctx_cap + want - 1) / want;
   len = (len + 63) / 64 * 64;
   if (want > 1 && len < 256) len = 256;

@@ -1,5 +1,7 @@
 """GPU parity of paged-cache decoding: the HIP kernels against the fp64
-oracle (oracle/decode.py) on identical seeded inputs.
+oracle (oracle/decode.py) on identical seeded inputs.  Key/value heads that
+serve up to 11 query rows run on the vector-ALU kernel, 12 or more on the
+matrix-core kernel; the cases cover both, with and without split contexts.
 
 Bars: the attention output bars, max |O_gpu - O_oracle| <= 2e-2 for bf16 and
 5e-3 for fp16, max |LSE_gpu - LSE_oracle| <= 1e-3; rows with no visible
@@ -89,6 +91,13 @@ CASES = [
     ("bf16", 128, 2, 32, 2, 1, 16, (40, 600)),       # 16 rows per key/value head: 2 slices
     ("bf16", 64, 1, 16, 2, 3, 16, (500,)),           # 24 rows: 3 slices
     ("bf16", 128, 1, 8, 8, 4, 16, (2,)),             # fewer cached tokens than query rows
+    ("bf16", 128, 1, 64, 1, 1, 16, (700,)),          # 64 rows: two 32-row slices
+    ("bf16", 128, 2, 2, 2, 1, 16, (5000, 3)),        # one row, split context
+    ("f16", 64, 2, 4, 2, 1, 16, (4500, 33)),         # two rows, split context
+    ("f16", 128, 2, 12, 4, 1, 32, (3000, 17)),       # three rows
+    ("bf16", 128, 2, 16, 2, 2, 16, (3000, 40)),      # 16 rows, split context (matrix core)
+    ("f16", 64, 3, 12, 1, 1, 16, (1, 129, 2500)),    # 12 rows (matrix core)
+    ("bf16", 128, 2, 40, 4, 1, 16, (900, 5000)),     # 10 rows: vector, 3 slices of 4
 ]
 
 

@@ -246,6 +246,10 @@ DECODE_WORKLOADS = {
     # four new tokens per request (causal among themselves)
     "decode_gqa_nq4": DecodeWorkload("decode_gqa_nq4", 32, 32, 8, 4, 128, "bf16", 16,
                                      512, 4096, seed=1102, extra_blocks=16),
+    # grouped heads, 8 query heads per key/value head (64 over 8, one new
+    # token), 16 requests of 1K-8K tokens
+    "decode_gqa8": DecodeWorkload("decode_gqa8", 16, 64, 8, 1, 128, "bf16", 16, 1024, 8192,
+                                  seed=1104, extra_blocks=16),
     # small case the oracle finishes at once
     "decode_small": DecodeWorkload("decode_small", 3, 4, 2, 2, 64, "bf16", 16, 1, 300,
                                    seed=1103, extra_blocks=5),
