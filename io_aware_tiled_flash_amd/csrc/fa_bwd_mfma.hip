@@ -176,39 +176,52 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dkacc[i] = dvacc[i] = f32x16{};
 
-  // Stream position u -> (query head, first row); past the end: a row
-  // beyond the sequence, whose loads zero-fill.
-  auto pair_of = [&](int u, int &bh, int &row0) __attribute__((always_inline)) {
-    if (u >= total) {
-      bh = b * H + hk * group;
-      row0 = S + BQ;
-      return;
-    }
-    const int j = u / nq;
-    bh = b * H + hk * group + j;
-    row0 = (qt_begin + u - j * nq) * BQ;
+  // Stream cursors (wave-uniform scalars, no division): the member j of the
+  // query-head group and the query tile qt of the tile being loaded and of
+  // the tile being finished.  j == group means past the end: a row beyond
+  // the sequence, whose loads zero-fill.
+  struct Cursor {
+    int j, qt;
   };
-  // Direct loads of tile u into stage st; d indexes this wave's LOADS loads.
-  auto dma = [&](int u, int st, int d) __attribute__((always_inline)) {
-    int bh, row0;
-    pair_of(u, bh, row0);
+  auto advance = [&](Cursor &c) __attribute__((always_inline)) {
+    const bool wrap = c.qt + 1 == qt_end;
+    c.qt = wrap ? qt_begin : c.qt + 1;
+    c.j += wrap ? 1 : 0;
+  };
+  auto row0_of = [&](const Cursor &c) __attribute__((always_inline)) {
+    return c.j < group ? c.qt * BQ : S + BQ;
+  };
+  Cursor ld{0, qt_begin}, fin{0, qt_begin};
+  // Sources of the tile under the load cursor, set once per tile.
+  struct Src {
+    u32x4 q, dout, stat;
+    int row0;
+  } src;
+  auto set_src = [&]() __attribute__((always_inline)) {
+    const int bh = b * H + hk * group + (ld.j < group ? ld.j : 0);
     const size_t q_off = (size_t)bh * (size_t)S * D;
+    src.q = rsrc_words((const uint16_t *)a.q + q_off, head_bytes);
+    src.dout = rsrc_words((const uint16_t *)a.dout + q_off, head_bytes);
+    const float *st = wave == 1 ? a.delta : a.lse;  // waves 2, 3: spare copies
+    src.stat = rsrc_words(st + (size_t)bh * S, (uint32_t)S * 4u);
+    src.row0 = row0_of(ld);
+  };
+  // Direct load d (of this wave's LOADS per tile) of the tile under the load
+  // cursor, into stage st.
+  auto dma = [&](int st, int d) __attribute__((always_inline)) {
     if (d < 2 * LPW) {
       const int i = d % LPW;
       const int blk = wave * LPW + i;
       const int pos = 64 * blk + lane;
       const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
-      const uint32_t o = (uint32_t)((row0 + r) * D + 8 * cc) * 2u;
+      const uint32_t o = (uint32_t)((src.row0 + r) * D + 8 * cc) * 2u;
       if (d < LPW)
-        load16_to_lds(rsrc_words((const uint16_t *)a.q + q_off, head_bytes), o,
-                      (uint32_t)(uintptr_t)&q_lds[st][64 * blk]);
+        load16_to_lds(src.q, o, (uint32_t)(uintptr_t)&q_lds[st][64 * blk]);
       else
-        load16_to_lds(rsrc_words((const uint16_t *)a.dout + q_off, head_bytes), o,
-                      (uint32_t)(uintptr_t)&do_lds[st][64 * blk]);
+        load16_to_lds(src.dout, o, (uint32_t)(uintptr_t)&do_lds[st][64 * blk]);
     } else {
-      const float *src = wave == 1 ? a.delta : a.lse;  // waves 2, 3: spare copies
-      load4_to_lds(rsrc_words(src + (size_t)bh * S, (uint32_t)S * 4u),
-                   (uint32_t)(row0 + lane) * 4u, (uint32_t)(uintptr_t)&stat_lds[st][wave][0]);
+      load4_to_lds(src.stat, (uint32_t)(src.row0 + lane) * 4u,
+                   (uint32_t)(uintptr_t)&stat_lds[st][wave][0]);
     }
   };
 
@@ -221,18 +234,15 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   u32x4 ppk[2][2], dspk[2];
   dpacc[0] = dpacc[1] = f32x16{};
 
-  // Tile u's rows: row0 + 8*(r/4) + 4*lg + (r%4) for accumulator register r.
-  auto edge_of = [&](int u) __attribute__((always_inline)) {
-    int bh, row0;
-    pair_of(u, bh, row0);
+  // The finished tile's rows: row0 + 8*(r/4) + 4*lg + (r%4) for
+  // accumulator register r.
+  auto edge_of = [&](int row0) __attribute__((always_inline)) {
     if (MASK == kMaskNone) return false;
     bool e = row0 < kw0 + 31;
     if (MASK == kMaskWindow) e = e || row0 + BQ - 1 > kw0 - 1 + a.window;
     return e;
   };
-  auto fix_mask = [&](int u, u32x4 (&pk)[2]) __attribute__((always_inline)) {
-    int bh, row0;
-    pair_of(u, bh, row0);
+  auto fix_mask = [&](int row0, u32x4 (&pk)[2]) __attribute__((always_inline)) {
     const int key = kw0 + lq;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -254,11 +264,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     constexpr int P = decltype(phase_c)::value;
     constexpr bool HAS_PREV = decltype(has_prev_c)::value, HAS_CUR = decltype(has_cur_c)::value;
     constexpr int par = P & 1;
-    constexpr int cur = P, prev = (P + NST - 1) % NST, ld = (P + PF) % NST;
+    constexpr int cur = P, prev = (P + NST - 1) % NST, ldst = (P + PF) % NST;
     const char *qc = (const char *)&q_lds[cur][0];
     const char *dc = (const char *)&do_lds[cur][0];
     const char *qp = (const char *)&q_lds[prev][0];
     const char *dp = (const char *)&do_lds[prev][0];
+    set_src();
     // ---- phase 1: S(u), dP(u) | dS(u-1) ----
     float dl[16];
     if (HAS_PREV) {
@@ -293,7 +304,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
       // direct loads of tile u+PF, spread over the phase
 #pragma unroll
       for (int d = 0; d < LOADS; ++d)
-        if ((d * NS1) / LOADS == st) dma(u + PF, ld, d);
+        if ((d * NS1) / LOADS == st) dma(ldst, d);
       if (HAS_PREV) {
 #pragma unroll
         for (int r = st * 16 / NS1; r < (st + 1) * 16 / NS1; ++r) {
@@ -358,9 +369,15 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (HAS_CUR && MASK != kMaskNone) {
-      if (edge_of(u)) fix_mask(u, ppk[par]);
+    advance(ld);
+    if (HAS_CUR) {
+      if (MASK != kMaskNone) {
+        const int row0 = row0_of(fin);
+        if (edge_of(row0)) fix_mask(row0, ppk[par]);
+      }
+      advance(fin);
     }
+    (void)u;
     // Tile u+1 has landed once only tile u+PF's loads are outstanding.
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (PF - 1)) : "memory");
     __builtin_amdgcn_s_barrier();
@@ -377,9 +394,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   using F = std::false_type;
   if (total > 0) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
+    for (int u = 0; u < PF; ++u) {
+      set_src();
 #pragma unroll
-      for (int d = 0; d < LOADS; ++d) dma(u, u, d);
+      for (int d = 0; d < LOADS; ++d) dma(u, d);
+      advance(ld);
+    }
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (PF - 1)) : "memory");
     __builtin_amdgcn_s_barrier();
     step(I0{}, F{}, T{}, 0);
