@@ -35,6 +35,10 @@ namespace {
 
 using namespace tile;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kMaxSplitLen = 4096;               // tokens per work-group at most
 constexpr int kMaxTable = kMaxSplitLen + 2;      // table entries one split can touch
@@ -47,6 +51,7 @@ constexpr int kMfmaRows = FA_DEC_MFMA_ROWS;      // query rows per key/value hea
 #define FA_DEC_MFMA_GROUPS 1024
 #endif
 constexpr int kMfmaGroups = FA_DEC_MFMA_GROUPS;  // work-groups the MFMA path aims for
+
 
 template <class Ty> struct Dot;
 template <> struct Dot<TBF16> {
@@ -299,22 +304,49 @@ __global__ __launch_bounds__(kThreads) void fa_decode_merge_kernel(DecodeArgs a)
   if (lane == 0) a.lse[row] = lse;
 }
 
-// Matrix-core variant, used when a key/value head serves many query rows
-// (grouped heads and several new tokens): 32 rows per work-group, padded.  It is
-// the forward kernel's decomposition with the keys gathered through the
-// block table: per wave and step, 32 keys; S^T = K Q^T with K loaded from the
-// cache straight into MFMA operand registers (lane: one key, 16 bytes of its
-// row), the running softmax over the 16 keys a lane holds for its row (and
-// the other 16 in the partner lane), and O^T += V^T P^T with V^T read by
-// ds_read_b64_tr_b16 from a wave-private LDS tile the wave fills from
-// registers.  The next step's rows are loaded while the current one computes.
-// Waves take every fourth step of the split and are merged through LDS at
-// the end, then the splits as in the vector kernel.
+// Matrix-core variant, for a key/value head serving many query rows (grouped
+// heads times new tokens): 16 keys and 16 query rows per wave step, on
+// v_mfma_f32_16x16x32 (scores S^T = K Q^T) and v_mfma_f32_16x16x16 (output
+// O^T += V^T P^T).  The score accumulator's layout (lane: one row, four
+// consecutive keys) is exactly the B operand of the output product, and one
+// transposing LDS read (ds_read_b64_tr_b16) gives each lane the four keys of
+// its V^T operand, so nothing is permuted.  K rows are gathered through the
+// block table straight into operand registers (lane: one key's 16-byte
+// chunks); V rows pass through a wave-private LDS tile.  Waves take every
+// fourth step of the split, with two register sets alternating so one step's
+// rows are in flight while the other computes, and merge through LDS at the
+// end; splits merge as in the vector kernel.  A step's operands take 32
+// registers, so three waves share a SIMD.
+template <class Ty> struct M16;
+template <> struct M16<TBF16> {
+  __device__ static inline f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                     __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+  }
+};
+template <> struct M16<TF16> {
+  __device__ static inline f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+};
+
 template <class Ty, int D>
-__global__ __launch_bounds__(kThreads, 1) void fa_decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NKS = D / 16, NDB = D / 32, KCH = D / 8;
-  constexpr int TK = 32;                           // keys per wave step
-  constexpr int VT_BYTES = TK * D * 2;             // one wave's V tile
+__global__ __launch_bounds__(kThreads, 3) void fa_decode_m16_kernel(DecodeArgs a) {
+  constexpr int NK = D / 32;                       // score MFMAs (32 d values each)
+  constexpr int NDB = D / 16;                      // output blocks of 16 d values
+  constexpr int KCH = D / 8;                       // 16-byte chunks per row
+  constexpr int NV = KCH / 4;                      // V chunks per lane per step
+  constexpr int TK = 16;                           // keys (and rows) per wave step
+  constexpr int VT_BYTES = TK * D * 2;
   static_assert(2 * TK * D * 4 <= 4 * VT_BYTES, "merge buffer must fit in the V tiles");
   __shared__ int tab[kMaxTable];
   __shared__ __attribute__((aligned(16))) char vt_raw[4 * VT_BYTES];
@@ -322,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_decode_mfma_kernel(DecodeArgs 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lq = lane & 31, lg = lane >> 5;
+  const int i16 = lane & 15, g4 = lane >> 4;
 
   const int pairs = a.B * a.Hkv;
   int rs = 0, base = blockIdx.x;
@@ -349,8 +381,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_decode_mfma_kernel(DecodeArgs 
     tab[e] = (v >= 0 && v < a.num_blocks) ? v : -1;
   }
 
-  // This lane's query row (lanes lq and lq + 32 share it).
-  const int rho = rs * TK + lq;
+  // This lane's row (shared by lanes i16, i16 + 16, i16 + 32, i16 + 48).
+  const int rho = rs * TK + i16;
   const bool row_ok = rho < rows_total;
   int out_row = 0, pos = -1;
   if (row_ok) {
@@ -358,124 +390,119 @@ __global__ __launch_bounds__(kThreads, 1) void fa_decode_mfma_kernel(DecodeArgs 
     out_row = (b * a.H + g * group + j) * a.n_q + i;
     pos = n - a.n_q + i;
   }
-  u32x4 qreg[NKS];
+  // Q^T as the B operand of S^T = K Q^T: row i16, d values 32*ks + 8*g4 ..
+  u32x4 qreg[NK];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qreg[ks] = row_ok ? *(const u32x4 *)((const uint16_t *)a.q + (size_t)out_row * D + 16 * ks +
-                                         8 * lg)
+  for (int ks = 0; ks < NK; ++ks)
+    qreg[ks] = row_ok ? *(const u32x4 *)((const uint16_t *)a.q + (size_t)out_row * D + 32 * ks +
+                                         8 * g4)
                       : u32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qreg[ks]));
-  const int min_pos = n - a.n_q;  // smallest query position of the request
+  for (int ks = 0; ks < NK; ++ks) asm volatile("" : "+a"(qreg[ks]));
+  const int min_pos = n - a.n_q;
   __syncthreads();
 
   const size_t blk_stride = (size_t)a.Hkv << sh;
   const uint16_t *kc = (const uint16_t *)a.k_cache + ((size_t)g << sh) * D;
   const uint16_t *vc = (const uint16_t *)a.v_cache + ((size_t)g << sh) * D;
   char *vt = vt_raw + wave * VT_BYTES;
-  const TileOffsets<D> off(lane);
+  // Transposing read of output block db: rows (keys) 4*g4 + (lane%16)/4,
+  // 4 values from column 16*db + 4*(lane%4); lane receives column
+  // 16*db + i16 of keys 4*g4 .. 4*g4 + 3.
+  // (The swizzle XORs every chunk-index bit of a row, so each block needs
+  // its own lane offset.)
+  const int tr_r = 4 * g4 + (i16 >> 2);
+  int tr_off[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    tr_off[db] = tr_r * (D * 2) + 16 * swz<D>(tr_r, 2 * db + ((lane & 3) >> 1)) + 8 * (lane & 1);
 
-  // Rows of step j's key lq: K operand chunks 2*ks + lg, V chunks 2*ks + lg.
-  // Every lane loads (a key that does not exist reads block 0's first row,
-  // always valid memory): loads under a branch would make the compiler wait
-  // for all of them before the next use of any.  Such keys are masked from
-  // the scores and their V rows are zeroed before use.
+  // Step j's key i16: K chunks (A operand, d = 32*ks + 8*g4) and V chunks
+  // 4*s + g4.  Every lane loads (a missing key reads block 0's first row,
+  // always valid memory); missing keys are masked and their V rows zeroed.
   struct Rows {
-    u32x4 k[NKS], v[NKS];
+    u32x4 k[NK], v[NV];
   };
   auto fetch = [&](int j) __attribute__((always_inline)) {
-    const int key = t0 + TK * j + lq;
+    const int key = t0 + TK * j + i16;
     int blk = -1;
     if (key < t1) blk = tab[(key >> sh) - first];
-    const size_t row = blk >= 0
-                           ? ((size_t)blk * blk_stride + (size_t)(key & bs_mask)) * D + 8 * lg
-                           : (size_t)(8 * lg);
+    const size_t row = blk >= 0 ? ((size_t)blk * blk_stride + (size_t)(key & bs_mask)) * D : 0;
     Rows out;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      out.k[ks] = __builtin_nontemporal_load((const u32x4 *)(kc + row + 16 * ks));
-      out.v[ks] = __builtin_nontemporal_load((const u32x4 *)(vc + row + 16 * ks));
-    }
+    for (int ks = 0; ks < NK; ++ks)
+      out.k[ks] = __builtin_nontemporal_load((const u32x4 *)(kc + row + 32 * ks + 8 * g4));
+#pragma unroll
+    for (int s2 = 0; s2 < NV; ++s2)
+      out.v[s2] = __builtin_nontemporal_load((const u32x4 *)(vc + row + 8 * (4 * s2 + g4)));
     return out;
   };
 
   float m = -INFINITY, l = 0.f;
-  f32x16 oacc[NDB];
+  f32x4 oacc[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float cl2 = a.scale_log2;
   const int n_steps = (t1 - t0 + TK - 1) / TK;
 
   auto body = [&](int j, const Rows &cur) __attribute__((always_inline)) {
-    // Keys of this step that exist (valid block, inside the split).
     const int tk = t0 + TK * j;
     bool key_ok;
     {
-      const int key = tk + lq;
+      const int key = tk + i16;
       key_ok = key < t1;
       if (key_ok) key_ok = tab[(key >> sh) - first] >= 0;
     }
-    const int kvalid = (int)(uint32_t)__builtin_amdgcn_ballot_w64(key_ok);  // bit k: key k
-    // V rows of step j into the wave's tile (row lq, chunk 2*ks + lg); rows of
-    // keys that do not exist are zero.
+    const int kvalid = (int)((uint32_t)__builtin_amdgcn_ballot_w64(key_ok) & 0xffffu);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 v = cur.v[ks];
-      if (kvalid != -1) v = key_ok ? v : u32x4{0, 0, 0, 0};
-      *(u32x4 *)(vt + lq * (D * 2) + 16 * swz<D>(lq, 2 * ks + lg)) = v;
+    for (int s2 = 0; s2 < NV; ++s2) {
+      u32x4 v = cur.v[s2];
+      if (kvalid != 0xffff) v = key_ok ? v : u32x4{0, 0, 0, 0};
+      *(u32x4 *)(vt + i16 * (D * 2) + 16 * swz<D>(i16, 4 * s2 + g4)) = v;
     }
-    f32x16 sacc = f32x16{};
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) sacc = Ty::mfma(cur.k[ks], qreg[ks], sacc);
-    float sv[16];
+    for (int ks = 0; ks < NK; ++ks) sacc = M16<Ty>::mfma32(cur.k[ks], qreg[ks], sacc);
+    // lane: keys 4*g4 + r (r = 0..3) of row i16
+    float sv[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = sacc[r] * cl2;
-    if (kvalid != -1 || tk + TK - 1 > min_pos) {  // some key hidden from some row
+    for (int r = 0; r < 4; ++r) sv[r] = sacc[r] * cl2;
+    if (kvalid != 0xffff || tk + TK - 1 > min_pos) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = 8 * (r >> 2) + 4 * lg + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int kr = 4 * g4 + r;
         const bool vis = ((kvalid >> kr) & 1) && tk + kr <= pos;
         if (!vis) sv[r] = -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-#pragma unroll
-    for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sv[r]), r + 1 < 16 ? sv[r + 1] : sv[r]);
-    mx = fmaxf(mx, wave_partner(mx));
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = mx > m + kTau ? mx : m;
-    if (__builtin_amdgcn_ballot_w64(m_new != m) != 0) {  // rare: move the offsets
+    if (__builtin_amdgcn_ballot_w64(m_new != m) != 0) {
       const float al = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
       l *= al;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= al;
+        for (int r = 0; r < 4; ++r) oacc[db][r] *= al;
       m = m_new;
     }
     const float mu = m == -INFINITY ? 0.f : m;
-    float pw[16];
+    float pw[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pw[r] = __builtin_amdgcn_exp2f(sv[r] - mu);
-    float ls = 0.f;
+    for (int r = 0; r < 4; ++r) pw[r] = __builtin_amdgcn_exp2f(sv[r] - mu);
+    l += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+    u32x2 ppk;
+    ppk[0] = Ty::pack2(pw[0], pw[1]);
+    ppk[1] = Ty::pack2(pw[2], pw[3]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ls += pw[r];
-    l += ls;
-    u32x4 ppk[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        ppk[kk][jj] = Ty::pack2(pw[8 * kk + 2 * jj], pw[8 * kk + 2 * jj + 1]);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        oacc[db] = Ty::mfma(off.tr_op(vt, kk, db), ppk[kk], oacc[db]);
+    for (int db = 0; db < NDB; ++db) {
+      const u32x2 va = lds_read_tr16((const FA_LDS void *)(vt + tr_off[db]));
+      oacc[db] = M16<Ty>::mfma16(va, ppk, oacc[db]);
+    }
   };
 
-  // Two register sets alternate (no copy between them: copying a loaded
-  // value would wait for its load), so one step's rows are always in flight
-  // while the other step computes.
   Rows ra = fetch(wave);
   for (int j = wave; j < n_steps; j += 8) {
     const Rows rb = fetch(j + 4);
@@ -484,59 +511,43 @@ __global__ __launch_bounds__(kThreads, 1) void fa_decode_mfma_kernel(DecodeArgs 
     if (j + 4 < n_steps) body(j + 4, rb);
   }
 
-  // Merge the four waves: 2 and 3 into 0 and 1, then 1 into 0.
-  const float lrow = l + wave_partner(l);
+  // Row sums over the row's four lanes, then the four waves (2, 3 into 0, 1;
+  // then 1 into 0) through LDS.
+  float lr = l + __shfl_xor(l, 16, 64);
+  lr += __shfl_xor(lr, 32, 64);
   float *mo = (float *)vt_raw;  // [2][TK rows][D] fp32, over the V tiles
   __syncthreads();
   auto put = [&](int slot) __attribute__((always_inline)) {
-    if (lg == 0) {
-      mrg_m[slot][lq] = m;
-      mrg_l[slot][lq] = lrow;
+    if (g4 == 0) {
+      mrg_m[slot][i16] = m;
+      mrg_l[slot][i16] = lr;
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *(float4 *)&mo[(slot * TK + lq) * D + 32 * db + 8 * q4 + 4 * lg] =
-            float4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2],
-                   oacc[db][4 * q4 + 3]};
+      *(float4 *)&mo[(slot * TK + i16) * D + 16 * db + 4 * g4] =
+          float4{oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]};
   };
-  float lr = lrow;
   auto take = [&](int slot) __attribute__((always_inline)) {
-    const float m2 = mrg_m[slot][lq], l2 = mrg_l[slot][lq];
+    const float m2 = mrg_m[slot][i16], l2 = mrg_l[slot][i16];
     const float mm = fmaxf(m, m2);
     const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
     const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
     lr = a1 * lr + a2 * l2;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v = *(const float4 *)&mo[(slot * TK + lq) * D + 32 * db + 8 * q4 + 4 * lg];
-        oacc[db][4 * q4 + 0] = a1 * oacc[db][4 * q4 + 0] + a2 * v.x;
-        oacc[db][4 * q4 + 1] = a1 * oacc[db][4 * q4 + 1] + a2 * v.y;
-        oacc[db][4 * q4 + 2] = a1 * oacc[db][4 * q4 + 2] + a2 * v.z;
-        oacc[db][4 * q4 + 3] = a1 * oacc[db][4 * q4 + 3] + a2 * v.w;
-      }
+    for (int db = 0; db < NDB; ++db) {
+      const float4 v = *(const float4 *)&mo[(slot * TK + i16) * D + 16 * db + 4 * g4];
+      oacc[db][0] = a1 * oacc[db][0] + a2 * v.x;
+      oacc[db][1] = a1 * oacc[db][1] + a2 * v.y;
+      oacc[db][2] = a1 * oacc[db][2] + a2 * v.z;
+      oacc[db][3] = a1 * oacc[db][3] + a2 * v.w;
+    }
     m = mm;
   };
   if (wave >= 2) put(wave - 2);
   __syncthreads();
   if (wave < 2) take(wave);
   __syncthreads();
-  if (wave == 1) {
-    if (lg == 0) {
-      mrg_m[0][lq] = m;
-      mrg_l[0][lq] = lr;
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *(float4 *)&mo[lq * D + 32 * db + 8 * q4 + 4 * lg] =
-            float4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2],
-                   oacc[db][4 * q4 + 3]};
-  }
+  if (wave == 1) put(0);
   __syncthreads();
   if (wave != 0 || !row_ok) return;
   take(0);
@@ -547,41 +558,36 @@ __global__ __launch_bounds__(kThreads, 1) void fa_decode_mfma_kernel(DecodeArgs 
   if (ns_b == 1) {
     uint16_t *orow = (uint16_t *)a.o + (size_t)out_row * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2 w;
-        w[0] = Ty::pack2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv);
-        w[1] = Ty::pack2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
-        *(u32x2 *)(orow + 32 * db + 8 * q4 + 4 * lg) = w;
-      }
-    if (lg == 0) a.lse[out_row] = lv;
+    for (int db = 0; db < NDB; ++db) {
+      u32x2 w;
+      w[0] = Ty::pack2(oacc[db][0] * inv, oacc[db][1] * inv);
+      w[1] = Ty::pack2(oacc[db][2] * inv, oacc[db][3] * inv);
+      *(u32x2 *)(orow + 16 * db + 4 * g4) = w;
+    }
+    if (g4 == 0) a.lse[out_row] = lv;
   } else {
     const size_t slot = (size_t)out_row * a.n_splits + split;
     float *wo = a.ws_o + slot * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *(float4 *)&wo[32 * db + 8 * q4 + 4 * lg] =
-            float4{oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv,
-                   oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv};
-    if (lg == 0) a.ws_lse[slot] = lv;
+      *(float4 *)&wo[16 * db + 4 * g4] =
+          float4{oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
+    if (g4 == 0) a.ws_lse[slot] = lv;
   }
 }
 
 template <class Ty, int D>
-bool run_decode_mfma(const DecodeArgs *a, const DecodePlan *p, hipStream_t stream, bool launch,
-                     LaunchInfo *info, hipError_t *err) {
+bool run_decode_m16(const DecodeArgs *a, const DecodePlan *p, hipStream_t stream, bool launch,
+                    LaunchInfo *info, hipError_t *err) {
   static char name[96];
-  snprintf(name, sizeof(name), "fa_decode_paged_mfma<%s,d%d,rows32>", Ty::kName, D);
+  snprintf(name, sizeof(name), "fa_decode_paged_m16<%s,d%d,rows16>", Ty::kName, D);
   info->name = name;
-  info->block_rows = 32;
+  info->block_rows = 16;
   info->threads = kThreads;
   if (!launch) return true;
   DecodeArgs args = *a;
   void *kargs[] = {&args};
-  *err = hipLaunchKernel((const void *)&fa_decode_mfma_kernel<Ty, D>, dim3((unsigned)p->grid),
+  *err = hipLaunchKernel((const void *)&fa_decode_m16_kernel<Ty, D>, dim3((unsigned)p->grid),
                          dim3(kThreads), kargs, 0, stream);
   if (*err != hipSuccess || p->n_splits == 1) return true;
   const int64_t rows = (int64_t)a->B * a->H * a->n_q;
@@ -617,7 +623,7 @@ bool decode_by_rows(const DecodeArgs *a, const DecodePlan *p, hipStream_t s, boo
     case 1: return run_decode<Ty, D, 1>(a, p, s, launch, info, err);
     case 2: return run_decode<Ty, D, 2>(a, p, s, launch, info, err);
     case 4: return run_decode<Ty, D, 4>(a, p, s, launch, info, err);
-    case 32: return run_decode_mfma<Ty, D>(a, p, s, launch, info, err);
+    case 16: return run_decode_m16<Ty, D>(a, p, s, launch, info, err);
   }
   return false;
 }
@@ -639,12 +645,12 @@ bool decode_plan(int d, int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t 
   if (d != 64 && d != 128) return false;
   const int64_t rows_total = (H / Hkv) * n_q;
   // A key/value head serving many query rows goes to the matrix-core kernel
-  // (32 rows per work-group); up to kMfmaRows - 1 rows stay on the vector
+  // (16 rows per work-group); up to kMfmaRows - 1 rows stay on the vector
   // ALUs, which measured faster there.  The vector kernel takes at most 4
   // rows per work-group: more rows slices (whose repeated cache reads hit
   // the shared L2) measured faster than 8-row work-groups, whose registers
   // cut the waves per SIMD from 5 to 3.
-  p->rows = rows_total <= 1 ? 1 : rows_total <= 2 ? 2 : rows_total < kMfmaRows ? 4 : 32;
+  p->rows = rows_total <= 1 ? 1 : rows_total <= 2 ? 2 : rows_total < kMfmaRows ? 4 : 16;
   p->row_slices = (int)((rows_total + p->rows - 1) / p->rows);
   // Enough work-groups to fill the chip several times over: split each
   // context when requests x key/value heads x row slices alone are too few.
@@ -652,7 +658,7 @@ bool decode_plan(int d, int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t 
   // ones; the matrix-core kernel runs one per CU and wants fewer, longer
   // ones (its per-work-group setup and merge are dearer).
   const int64_t units = B * Hkv * p->row_slices;
-  const int64_t target = p->rows == 32 ? kMfmaGroups : 2048;
+  const int64_t target = p->rows >= 16 ? kMfmaGroups : 2048;
   const int64_t want = units >= target ? 1 : (target + units - 1) / units;
   int64_t len = (ctx_cap + want - 1) / want;
   len = (len + 63) / 64 * 64;
