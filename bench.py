@@ -43,20 +43,21 @@ CSRC = os.path.join(ROOT, "io_aware_tiled_flash_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-# The sources the forward matrix-core kernel is compiled from: a committed
-# counter summary is only used while these are unchanged.
+# The sources each measured kernel is compiled from: a committed counter
+# summary is only used while these are unchanged.
 FWD_SOURCES = ("fa_fwd_mfma.hip", "fa_gfx950.h", "fa_internal.h")
+DECODE_SOURCES = ("fa_decode.hip", "fa_tile_ops.h", "fa_gfx950.h", "fa_internal.h")
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(sources=FWD_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in FWD_SOURCES:
+    for f in sources:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, sources=FWD_SOURCES):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources; otherwise None."""
     path = os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
@@ -67,7 +68,7 @@ def measured_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             key, _, val = line.partition(":")
             vals[key.strip()] = val.strip()
-    if vals.get("kernel_source_digest") != kernel_source_digest():
+    if vals.get("kernel_source_digest") != kernel_source_digest(sources):
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
@@ -224,7 +225,8 @@ def bench_decode(args) -> int:
                                                          " + fa_decode_merge_kernel")},
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, DECODE_SOURCES),
                      "scope": "whole call (one launch without splits, two with)"},
         "attention_TFLOPs": round(tflops, 2),
     }
