@@ -613,7 +613,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_s_barrier();
   };
 
-  asm volatile("" ::"s"(rk), "s"(rv), "s"(a.dq));
+  // Settle the loads the loop reads (kernel arguments, the row's statistics)
+  // before it: a compiler-tracked load still pending at a use inside the
+  // loop makes it wait for vmcnt(0) there, which also drains the direct loads
+  // that run ahead.
+  asm volatile("" ::"s"(rk), "s"(rv), "s"(a.dq), "v"(lse2), "v"(drow));
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
