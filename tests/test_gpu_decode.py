@@ -181,7 +181,7 @@ def test_decode_outputs_do_not_touch_neighbours():
 
 
 @pytest.mark.parametrize("name", ["decode_small", "decode_opt13b_b256", "decode_gqa_long",
-                                  "decode_gqa_nq4"])
+                                  "decode_gqa_nq4", "decode_gqa8", "decode_gqa_b256"])
 def test_decode_workloads(name):
     """The named workloads at full size, launched as the benchmark launches
     them; every head and row of sampled requests against the oracle."""

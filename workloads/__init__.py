@@ -250,6 +250,10 @@ DECODE_WORKLOADS = {
     # token), 16 requests of 1K-8K tokens
     "decode_gqa8": DecodeWorkload("decode_gqa8", 16, 64, 8, 1, 128, "bf16", 16, 1024, 8192,
                                   seed=1104, extra_blocks=16),
+    # grouped heads at serving scale: 256 requests of up to 4K tokens, 32 query
+    # heads over 8 key/value heads (about 2 GB of cache per step)
+    "decode_gqa_b256": DecodeWorkload("decode_gqa_b256", 256, 32, 8, 1, 128, "bf16", 16, 1,
+                                      4096, seed=1105, extra_blocks=64),
     # small case the oracle finishes at once
     "decode_small": DecodeWorkload("decode_small", 3, 4, 2, 2, 64, "bf16", 16, 1, 300,
                                    seed=1103, extra_blocks=5),
