@@ -51,6 +51,14 @@ constexpr int kMfmaRows = FA_DEC_MFMA_ROWS;      // query rows per key/value hea
 #define FA_DEC_MFMA_GROUPS 1024
 #endif
 constexpr int kMfmaGroups = FA_DEC_MFMA_GROUPS;  // work-groups the MFMA path aims for
+#ifndef FA_DEC_VALU_GROUPS
+#define FA_DEC_VALU_GROUPS 4096
+#endif
+constexpr int kValuGroups = FA_DEC_VALU_GROUPS;  // work-groups the vector path aims for
+#ifndef FA_DEC_MIN_SPLIT
+#define FA_DEC_MIN_SPLIT 1024
+#endif
+constexpr int kMinSplit = FA_DEC_MIN_SPLIT;      // shortest split worth its merge
 
 
 template <class Ty> struct Dot;
@@ -665,16 +673,17 @@ bool decode_plan(int d, int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t 
   p->rows = rows_total <= 1 ? 1 : rows_total <= 2 ? 2 : rows_total < kMfmaRows ? 4 : 16;
   p->row_slices = (int)((rows_total + p->rows - 1) / p->rows);
   // Enough work-groups to fill the chip several times over: split each
-  // context when requests x key/value heads x row slices alone are too few.
-  // The vector kernel runs several work-groups per CU and wants many short
-  // ones; the matrix-core kernel runs one per CU and wants fewer, longer
-  // ones (its per-work-group setup and merge are dearer).
+  // context when requests x key/value heads x row slices alone are too few,
+  // but never into pieces shorter than kMinSplit tokens (the merge grows with
+  // the number of pieces).  The vector kernel runs up to five work-groups per
+  // CU and aims for 4096; the matrix-core kernel, three, and aims for 1024.
+  // Both measured best over the decode workloads.
   const int64_t units = B * Hkv * p->row_slices;
-  const int64_t target = p->rows >= 16 ? kMfmaGroups : 2048;
+  const int64_t target = p->rows >= 16 ? kMfmaGroups : kValuGroups;
   const int64_t want = units >= target ? 1 : (target + units - 1) / units;
   int64_t len = (ctx_cap + want - 1) / want;
   len = (len + 63) / 64 * 64;
-  if (want > 1 && len < 256) len = 256;
+  if (want > 1 && len < kMinSplit) len = kMinSplit;
   if (len < 64) len = 64;
   if (len > kMaxSplitLen) len = kMaxSplitLen;
   p->split_len = (int)len;

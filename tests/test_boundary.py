@@ -249,21 +249,23 @@ def test_decode_workspace_rules():
     assert _ws(B=256, H=40, Hkv=40, max_ctx=2048, max_blocks=128) == 0
     # few long requests: split, and the workspace holds a row of d + 1 floats
     # per (query row, split)
-    need = _ws(B=1, H=8, Hkv=2, max_ctx=1024)
+    long = dict(B=1, H=8, Hkv=2, max_ctx=8192, max_blocks=512)
+    need = _ws(**long)
     assert need > 0 and need % (1 * 8 * 1 * 129 * 4) == 0
     n_splits = need // (8 * 129 * 4)
     assert n_splits >= 2
-    assert _ws(B=1, H=8, Hkv=2, max_ctx=2 * 1024, max_blocks=128) >= need
+    assert _ws(**dict(long, max_ctx=16384, max_blocks=1024)) >= need
     # max_ctx beyond what the table can hold changes nothing
     assert _ws(max_ctx=10 ** 6) == _ws(max_ctx=64 * 16)
-    # a needed workspace that is missing or too small is refused
-    st = _call_decode(B=1, workspace=0)
+    # a needed workspace that is missing or too small is refused (these sizes
+    # need one, so nothing is launched with the fake pointers)
+    st = _call_decode(workspace=0, **long)
     assert st == fa.FA_EINVAL and "workspace" in fa.fa_last_error()
-    st = _call_decode(B=1, workspace_bytes=need - 4)
+    st = _call_decode(workspace_bytes=need - 4, **long)
     assert st == fa.FA_EINVAL and "too small" in fa.fa_last_error()
-    st = _call_decode(B=1, workspace=A + 16 * MB + 1024, d=96)
+    st = _call_decode(workspace=A + 16 * MB + 1024, d=96, **long)
     assert st == fa.FA_EUNSUPPORTED  # size checks come first; nothing launched
-    st = _call_decode(B=1, workspace=A + 16 * MB + 1024)
+    st = _call_decode(workspace=A + 16 * MB + 1024, **long)
     assert st == fa.FA_EINVAL and "workspace overlaps" in fa.fa_last_error()
 
 
