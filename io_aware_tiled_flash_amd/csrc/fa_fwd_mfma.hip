@@ -5,10 +5,12 @@
 // sections "Online softmax: correct as you go" and "The tiled forward pass";
 // aicomputerinstitute.com grade-12 flash-attention chapter, section "Tiling
 // and the running (online) softmax").  Per query row the kernel keeps a
-// running maximum m, a running denominator l and an unnormalised fp32 output
-// accumulator; for every visible key tile it rescales l and the accumulator by
-// exp(m_old - m_new) when the maximum moves, adds the tile's exponentiated
-// scores, and divides by l once after the last tile.  Score and probability
+// running offset m (the role of the running maximum), a running denominator
+// l and an unnormalised fp32 output accumulator; for every visible key tile
+// it adds the tile's exponentiated scores exp(s - m), moves m up to the
+// tile's maximum (rescaling l and the accumulator by exp(m_old - m_new)) when
+// those weights would grow too large, and divides by l once after the last
+// tile.  Score and probability
 // tiles live only in registers.  The work split over the query sequence (one
 // work-group per query tile, per batch and head) follows the same chapter's
 // section "What FlashAttention-2 changed"; each wavefront owns distinct query
@@ -33,9 +35,10 @@
 //     directly as the B operand (a contraction's summation order is free as
 //     long as both operands agree on it);
 //   * with NH = 2 each K or V operand read from LDS feeds two MFMAs (one per
-//     half), halving LDS traffic per flop, and the loop body is ordered
-//     S_0, {S_1 | softmax_0}, {O_0 | softmax_1}, O_1 so that one half's
-//     vector-ALU softmax can issue while the other half's MFMAs run;
+//     half), halving LDS traffic per flop;
+//   * the vector-ALU softmax work of a tile is spread over the MFMAs of two
+//     phases (see the tile loop below), so that the matrix core runs while
+//     the wave issues it;
 //   * tiles are loaded PF tiles ahead of the math into free LDS stages (PF+1
 //     for K, PF+2 for V because the PV products lag one tile), which hides
 //     the L2/HBM latency behind several tiles of math; one barrier per tile;
@@ -45,12 +48,17 @@
 //     a band edge of a wave's rows;
 //   * scores are scaled into base 2 (scale * log2 e) so that every exponential
 //     is one v_exp_f32, with the scale folded into the exponent's FMA;
-//   * lazy rescaling: the running offset m is only moved when a row's maximum
-//     exceeds it by more than TAU (base-2 units); until then exponentials are
-//     taken against the stale m, so unnormalised weights stay below 2^TAU.
-//     The final O = acc / l and LSE = m + log l use the same m, so the result
-//     is unchanged up to rounding (the deferred-rescaling idea of the
-//     "What FlashAttention-2 changed" section);
+//   * lazy offset: the exponentials of a tile are taken against the row's
+//     current offset m without first looking at the tile's maximum.  Only a
+//     lane whose tile weight sum exceeds a cap (2^32 for bf16 weights, which
+//     share fp32's exponent range; 2^8 for fp16), or a row that has no
+//     offset yet, sends the wave to a rare branch that takes the true row
+//     maximum of the tile, moves m up to it, rescales the accumulator and
+//     denominator by exp(m_old - m_new) and recomputes the tile's weights.
+//     Every final O = acc / l and LSE = m + log l uses one m per row, so the
+//     result is unchanged up to rounding (the deferred-rescaling idea of the
+//     "What FlashAttention-2 changed" section, taken one step further: the
+//     common path computes no row maximum at all);
 //   * l accumulates the fp32 weights (before they are rounded to the input
 //     dtype for the PV product), so the logsumexp is not limited by bf16
 //     precision;
@@ -68,15 +76,20 @@
 namespace fa {
 namespace {
 
-constexpr float TAU = 8.0f;  // max growth (base 2) tolerated before rescaling
+using namespace tile;
+
+// Offset-move cap: a lane's tile weight sum above it sends the wave to the
+// offset update.  bf16 weights share fp32's exponent range, so they may grow
+// to 2^32 before the offset has to move (the accumulator then stays below
+// 2^52 times the largest |V|); fp16 weights must stay below 65504, so they
+// move it at 2^8.
+template <class Ty> struct WeightCap;
+template <> struct WeightCap<TBF16> { static constexpr float value = 4294967296.0f; };
+template <> struct WeightCap<TF16> { static constexpr float value = 256.0f; };
+
 #ifndef FA_RPD
 #define FA_RPD 3
 #endif
-#ifndef FA_UA_PRE
-#define FA_UA_PRE 6
-#endif
-
-using namespace tile;
 
 template <class Ty, int D, int MASK, int NW, int BC, int NH, int PF>
 __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   f32x16 oacc[NH][NDB];
   f32x16 sacc[NH][NKB];
   u32x4 pk[NH][NPS];  // packed weights of the previous tile, awaiting their PV product
-  float m[NH], m_prev[NH], l[NH];
+  float m[NH], l[NH];
   float m_use[NH], lpart[NH];  // offset the exponent arguments use; a tile's weight sum
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -190,7 +203,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NPS; ++i) pk[h][i] = u32x4{};
     m[h] = -INFINITY;  // running offset, base 2 (equal in lanes q and q^32)
-    m_prev[h] = -INFINITY;  // the offset before the current tile's update
     l[h] = 0.f;        // this lane's share of the running denominator
     m_use[h] = 0.f;
     lpart[h] = -0.f;
@@ -261,27 +273,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     }
   };
 
-  // Rescale where some lane's offset moved.  Rare once the running maxima
-  // settle (see TAU), so it sits at the end of a tile, where its branch does
-  // not split the MFMA/ALU interleaving of the phases.  Both the accumulator and the denominator are rescaled here, by
-  // alpha = exp2(old offset - new offset) (0 from a row with no visible key
-  // so far, whose accumulator is still 0), so the common path computes no
-  // factor at all.  One test covers all halves (a factor of 1 is exact).
-  auto rescale = [&]() __attribute__((always_inline)) {
-    bool any_change = m[0] != m_prev[0];
-#pragma unroll
-    for (int h = 1; h < NH; ++h) any_change = any_change || m[h] != m_prev[h];
-    if (__any(any_change)) {
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const float alpha = __builtin_amdgcn_exp2f(m_prev[h] - m_use[h]);
-        l[h] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[h][db] *= alpha;
-      }
-    }
-  };
-
   // Elementwise mask of the raw scores (tiles straddling a band edge):
   // invisible (query, key) pairs become -inf.
   auto apply_mask = [&](int k0) __attribute__((always_inline)) {
@@ -298,27 +289,20 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     }
   };
 
-  // Online softmax, in pieces that the pipeline below places next to MFMA work.
+  // Online softmax, in units that the pipeline below places between MFMAs.
   // Contraction step kk of the PV product covers, in each lane, the 8 scores
   // sc[kk/2][8*(kk%2) .. +7]; weights are exp2(c*s - offset).
-  // finish(h): l <- l + (sum of the tile's weights).
-  auto sm_finish = [&](int h) __attribute__((always_inline)) { l[h] += lpart[h]; };
-
-  // Software pipeline over key tiles (t = current tile):
-  //   phase A: S(t) = K_t Q^T on MFMA, next to the exponentials of tile t-1:
-  //            weights from the exponent arguments saved by phase B of t-1,
-  //            packed for the PV product, and the denominators' update;
-  //   phase B: O += V_{t-1}^T P(t-1)^T on MFMA (both halves share each V
-  //            operand), next to the rest of tile t's softmax: row maxima,
-  //            offsets and factors of every half, and the exponent arguments
-  //            c*s - offset of every score;
-  //   then the rare rescale of O by tile t's factors, which must land after
-  //   the products of tile t-1 and before those of tile t.
-  // Each phase is one basic block whose ALU work is independent of the MFMAs
-  // it issues beside, so the vector ALU and the matrix core work at the same
-  // time inside one wave, and the two phases carry similar ALU loads.  Only
-  // exponent arguments cross from one tile to the next, so no score
-  // registers are copied along the loop.
+  //   argument unit (phase B of tile t): four exponent arguments c*s - offset
+  //     of one half and step, from the tile's scores;
+  //   weight unit: two weights from saved arguments, packed for the PV
+  //     product and added to the lane's sums.  The weights of the first NPS/2
+  //     steps (at most UAB units) are made in the second half of phase B of
+  //     tile t, once the products of tile t-1 have read those registers; the
+  //     rest in phase A of tile t+1;
+  //   finish (end of phase A of tile t+1): the lane's tile sums, the test
+  //     that sends the wave to the offset update, and the denominators.
+  // Only exponent arguments and weights cross from one tile to the next, so
+  // no score registers are copied along the loop.
   float xdef[NH][NPS][8];
 #pragma unroll
   for (int h = 0; h < NH; ++h)
@@ -327,19 +311,23 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) xdef[h][i][j] = -INFINITY;
 
-  // Phase A work, in units: unit u makes the weights of pair j = u % 4 of
-  // step kk = (u / 4) % NPS of half h = u / (4 * NPS) from the saved
-  // exponent arguments; a_finish folds the sums into the denominators.
-  constexpr int UA = NH * NPS * 4;
+  constexpr int KKB = NPS / 2;                 // steps whose weights phase B may make
+  constexpr int UAB_ALL = NH * KKB * 4;
+  constexpr int UAB = 8 < UAB_ALL ? 8 : UAB_ALL;  // weight units phase B makes
+  constexpr int UA = NH * NPS * 4 - UAB;       // weight units left to phase A
+  constexpr float CAP = WeightCap<Ty>::value;
   float s4a[NH][4];
-  auto a_start = [&]() __attribute__((always_inline)) {
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s4a[h][j] = -0.f;
+  auto sums_start = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int j = 0; j < 4; ++j) s4a[h][j] = -0.f;  // -0 + x == x folds away
   };
-  auto a_unit = [&](int u) __attribute__((always_inline)) {
-    const int h = u / (4 * NPS), kk = (u / 4) % NPS, j = u % 4;
+  auto weight_unit = [&](int h, int kk, int j) __attribute__((always_inline)) {
     const float p0 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j]);
     const float p1 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j + 1]);
     pk[h][kk][j] = Ty::pack2(p0, p1);
@@ -347,85 +335,103 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     pin(pk[h][kk][j]);
     pin(s4a[h][j]);
   };
+  // Weight units in step-major order: r -> (half (r/4) % NH, step r/(4 NH),
+  // pair r % 4); phase B makes r < UAB, phase A the rest.
+  auto b_weight_unit = [&](int r) __attribute__((always_inline)) {
+    weight_unit((r / 4) % NH, r / (4 * NH), r % 4);
+  };
+  auto a_unit = [&](int u) __attribute__((always_inline)) { b_weight_unit(u + UAB); };
+
+  // Offset update, off the common path.  The weights above were taken
+  // against the current offset without looking at the tile's maximum.  A
+  // lane whose tile sum exceeds CAP may hold a weight above CAP, and a row
+  // that has seen no visible key yet has no offset; either sends the wave
+  // here.  The row maximum t of the exponent arguments is taken over both
+  // lanes of each row; a row with an offset moves it up by max(t, 0),
+  // scaling its accumulator and denominator by exp2(-shift); a row without
+  // one takes the maximum itself (its accumulator and denominator are still
+  // 0).  The tile's weights are then recomputed against the new offset, so
+  // every weight of a row stays at most CAP times its offset's weight.  The
+  // accumulator holds the tiles before this one (their products were all
+  // issued in the phase before), so the rescale and the recomputed weights
+  // agree.
+  auto settle = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      float t = xdef[h][0][0];
+#pragma unroll
+      for (int kk = 0; kk < NPS; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t = fmaxf(t, xdef[h][kk][j]);
+      t = fmaxf(t, wave_partner(t));
+      const bool fresh = m[h] == -INFINITY;
+      const float shift = fresh ? (t == -INFINITY ? 0.f : t) : fmaxf(t, 0.f);
+      const float alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(-shift);
+      if (!(fresh && t == -INFINITY)) m[h] = m_use[h] + shift;
+      m_use[h] = m[h] == -INFINITY ? 0.f : m[h];
+      float sum = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NPS; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j] - shift);
+          const float p1 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j + 1] - shift);
+          pk[h][kk][j] = Ty::pack2(p0, p1);
+          sum += p0 + p1;
+        }
+      lpart[h] = sum;
+      l[h] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[h][db] *= alpha;
+    }
+  };
   auto a_finish = [&]() __attribute__((always_inline)) {
+    bool trig = false;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       lpart[h] = (s4a[h][0] + s4a[h][1]) + (s4a[h][2] + s4a[h][3]);
-      sm_finish(h);
+      trig = trig || lpart[h] > CAP || m[h] == -INFINITY;
+    }
+    if (__any(trig)) settle();
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      l[h] += lpart[h];
       pin(l[h]);
     }
   };
 
-  // Phase B work, in units: 4 * NH partial row maxima (quarter q of half h),
-  // NH head finishes (exchange with lane ^ 32, new offset and factor), then
-  // 2 * NPS * NH groups of four exponent arguments.
-  // The row maximum is one max3 chain per half: unit q of half h folds the
-  // scores 4q .. 4q+3 of every 32-key block into it.
-  constexpr int UB_MAX = 4 * NH, UB_FIN = NH, UB_ARG = 2 * NPS * NH;
-  constexpr int UB = UB_MAX + UB_FIN + UB_ARG;
-  float tb[NH];
+  // Argument units, in step-major order: u -> (step u / (2 NH), half
+  // (u / 2) % NH, four arguments 4 * (u % 2) ..), so the first steps'
+  // arguments are ready before their weight units.
+  constexpr int UB = 2 * NPS * NH;
   auto b_unit = [&](int u) __attribute__((always_inline)) {
-    if (u < UB_MAX) {
-      const int h = u / 4, q = u % 4;
-      float t = q == 0 ? sacc[h][0][0] : tb[h];
+    const int kk = u / (2 * NH), h = (u / 2) % NH, part = u % 2;
+    const int kb = kk >> 1, base = 8 * (kk & 1) + 4 * part;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const int r = 4 * q + i;
-          t = (q == 0 && kb == 0 && i == 0) ? fmaxf(t, sacc[h][kb][r + 1])
-                                            : fmaxf(fmaxf(t, sacc[h][kb][r]), sacc[h][kb][r + 1]);
-        }
-      tb[h] = t;
-      pin(tb[h]);
-    } else if (u < UB_MAX + UB_FIN) {
-      const int h = u - UB_MAX;
-      float tmax = tb[h];
-      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, tmax),
-                                                       __builtin_bit_cast(uint32_t, tmax),
-                                                       false, false);
-      tmax = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
-                   __builtin_bit_cast(float, (uint32_t)sw[1])) * c;  // c > 0 keeps order
-      const float m_old = m[h];
-      const float m_new = tmax > m_old + TAU ? tmax : m_old;
-      // A row with no visible key so far keeps m = -inf; its exponent
-      // arguments use a finite stand-in, so masked scores still give 0.
-      m_use[h] = fmaxf(m_new, -1e30f);
-      m_prev[h] = m_old;
-      m[h] = m_new;
-      pin(m_use[h]);
-    } else {
-      const int v = u - UB_MAX - UB_FIN;
-      const int h = v / (2 * NPS), kk = (v / 2) % NPS, part = v % 2;
-      const int kb = kk >> 1, base = 8 * (kk & 1) + 4 * part;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xdef[h][kk][4 * part + i] = fmaf(sacc[h][kb][base + i], c, -m_use[h]);
-        pin(xdef[h][kk][4 * part + i]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      xdef[h][kk][4 * part + i] = fmaf(sacc[h][kb][base + i], c, -m_use[h]);
+      pin(xdef[h][kk][4 * part + i]);
     }
   };
 
   // One tile, software-pipelined (t = this tile):
-  //   phase A: S(t) = K_t Q^T on MFMA, next to the weights of tile t-1
-  //            (phase A units), the denominators' update and the direct
-  //            loads of tile t+PF;
-  //   phase B: O += V_{t-1}^T P(t-1)^T on MFMA, next to the softmax head of
-  //            tile t (phase B units): row maxima, offsets, factors and the
-  //            exponent arguments c*s - offset of every score;
-  //   then the rare rescale of O by tile t's factors, which must land after
-  //   the products of tile t-1 and before those of tile t.
-  // Both phases are written as a sequence of steps (operand read one step
+  //   phase A: S(t) = K_t Q^T on MFMA, next to the remaining weight units of
+  //            tile t-1, its finish (offset test and the rare update) and
+  //            the direct loads of tile t+PF;
+  //   phase B: O += V_{t-1}^T P(t-1)^T on MFMA (both halves share each V
+  //            operand), next to the argument units of tile t in its first
+  //            half and tile t's first weight units in its second half,
+  //            after the products that read those weight registers.
+  // Both phases are written as a sequence of steps (operand read RPD steps
   // ahead, one MFMA, its share of the ALU units) separated by scheduling
   // fences, so the instruction stream alternates matrix and vector work in
   // this order: the matrix core runs each MFMA while the wave issues the ALU
-  // work behind it.  Only exponent arguments cross from one tile to the
-  // next, so no score registers are copied along the loop.
+  // work behind it.
   constexpr int NSA = NKS * NKB, MA = NSA * NH;  // score steps, MFMAs
   constexpr int NSB = NPS * NDB, MB = NSB * NH;  // product steps, MFMAs
   constexpr int NDMA = 2 * LOADS_PER_WAVE;       // direct loads per tile
   constexpr int RPD = FA_RPD;                    // operand reads run RPD steps ahead
-  constexpr int UA_PRE = FA_UA_PRE < UA ? FA_UA_PRE : UA;  // units before the first MFMA
+  constexpr int UA_PRE = 1 < UA ? 1 : UA;        // units before the first MFMA
   // Tile with stage phase P = it % NST: K in stage P, the previous tile's V
   // in stage P-1, loads of tile it+PF into stage P+PF.
   auto tile = [&](bool masked, auto phase_c, int k0, int lkt) __attribute__((always_inline)) {
@@ -451,7 +457,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     auto dma_slot = [](int d) constexpr { return 2 * d + 1; };
     static_assert(2 * NDMA <= MA, "direct loads must fit between the score MFMAs");
     // ---- phase A ----
-    a_start();
     u32x4 kop[RPD + 1];
 #pragma unroll
     for (int st = 0; st < RPD && st < NSA; ++st) kop[st] = read_k(kl, st);
@@ -485,6 +490,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase B ----
     if (masked) apply_mask(k0);  // per-wave scalar branch at a fence point
+    sums_start();
 #pragma unroll
     for (int st = 0; st < NSB; ++st) {
       if (st + RPD < NSB) vop[(st + RPD) % (RPD + 1)] = read_v(vl, st + RPD);
@@ -493,12 +499,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       for (int h = 0; h < NH; ++h) {
         const int mi = st * NH + h;
         oacc[h][db] = Ty::mfma(vop[st % (RPD + 1)], pk[h][kk], oacc[h][db]);
+        if (mi < MB / 2) {
 #pragma unroll
-        for (int u = mi * UB / MB; u < (mi + 1) * UB / MB; ++u) b_unit(u);
+          for (int u = mi * UB / (MB / 2); u < (mi + 1) * UB / (MB / 2); ++u) b_unit(u);
+        } else {
+          const int q = mi - MB / 2;
+#pragma unroll
+          for (int r = q * UAB / (MB / 2); r < (q + 1) * UAB / (MB / 2); ++r) b_weight_unit(r);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    rescale();  // tile t's factors, after the products of tile t-1
   };
 
   // Zero the V stage that the first tile's (empty) pending product reads, so
@@ -561,8 +572,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     step(std::integral_constant<int, 2>{}, kt + 2);
     step(std::integral_constant<int, 3>{}, kt + 3);
   }
-  // The last tile: its weights, then its PV products.
-  a_start();
+  // The last tile: its remaining weights, then its PV products.
 #pragma unroll
   for (int u = 0; u < UA; ++u) a_unit(u);
   a_finish();

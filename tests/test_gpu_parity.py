@@ -180,6 +180,27 @@ def test_scale_values(scale):
     _check_full(q, k, v, "causal", None, scale, "f16", f"scale={scale}")
 
 
+@pytest.mark.parametrize("dtype,jump", [("bf16", 26.0), ("f16", 7.0)])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("mask", ["none", "causal", "window"])
+def test_offset_moves(dtype, jump, d, mask):
+    """Scores that climb (and fall) in 32-key plateaus.  The kernel lets a
+    row's unnormalised weights grow up to 2^32 (bf16 weights) or 2^8 (fp16)
+    before it moves the row's offset; steps of 1.5 * jump (natural units)
+    exceed that, steps of 0.5 * jump do not, and some steps go down, so rows
+    move their offset and rescale their accumulator several times, with
+    earlier keys still contributing."""
+    S = 300
+    q, k, v = make_inputs(1, 2, S, d, dtype, seed=40 + d)
+    scale = 1.0 / math.sqrt(d)
+    blk = np.arange(S) // 32
+    level = jump * (blk % 5) - 0.5 * jump * (blk % 2)
+    q[..., 0] = 1.0
+    k[..., 0] = torch.tensor(level / scale, dtype=torch.float32).to(k.dtype)
+    _check_full(q, k, v, mask, 50 if mask == "window" else None, scale, dtype,
+                f"offset moves {dtype} d={d} {mask}")
+
+
 # --------------------------------------------------------------------------
 # special cases with closed forms
 # --------------------------------------------------------------------------
