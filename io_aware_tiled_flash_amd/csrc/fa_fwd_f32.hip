@@ -2,11 +2,18 @@
 //
 // Same online-softmax tiling as the bf16/fp16 kernel ("FlashAttention: Why
 // Tiling Attention Makes Transformers Fast Without Changing the Result",
-// section "The tiled forward pass"), written for fp32 on the vector ALUs:
-// one lane owns one query row (its Q row and fp32 output accumulator sit in
-// VGPRs), K and V tiles of 32 keys are staged in LDS and read back as
-// wave-wide broadcasts.  fp32 exists for exactness checks rather than speed:
-// the matrix-core path is bf16/fp16.
+// section "The tiled forward pass"), written for fp32 on the vector ALUs.
+// A work-group owns 64 query rows; each of its four waves holds all 64 rows
+// (one lane per row: its Q row and fp32 output accumulator in registers) and
+// runs the online softmax over every fourth key tile of the visible range,
+// staging its 32-key K and V tiles in its own LDS buffers and reading them
+// back as wave-wide broadcasts.  The four partial states (m, l, O) of a row
+// are then merged with the same rescaling algebra the online softmax uses
+// between tiles (the split over the key sequence of the grade-12 chapter's
+// section "What FlashAttention-2 changed"): m = max m_w,
+// l = sum l_w exp(m_w - m), O = sum O_w exp(m_w - m), then O / l once.
+// fp32 exists for exactness checks rather than speed: the matrix-core path
+// is bf16/fp16.
 #include "fa_internal.h"
 
 #include <math.h>
@@ -22,13 +29,28 @@ __device__ inline bool key_visible(int key, int row, int S, int window) {
   return key <= row && key > row - window;
 }
 
-template <int D, int MASK>
-__global__ __launch_bounds__(64, 1) void fa_fwd_f32_kernel(FwdArgs a) {
-  constexpr int BR = 64, BC = 32, D4 = D / 4;
-  __shared__ float4 k_lds[BC * D4];
-  __shared__ float4 v_lds[BC * D4];
+// Make this wave's LDS writes visible to its own later reads (and keep the
+// compiler from moving LDS accesses across).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
 
-  const int tid = threadIdx.x;
+constexpr int kF32Waves = 4, kF32Rows = 64, kF32Keys = 32;
+
+template <int D, int MASK>
+__global__ __launch_bounds__(kF32Waves * 64, 1) void fa_fwd_f32_kernel(FwdArgs a) {
+  constexpr int NW = kF32Waves, BR = kF32Rows, BC = kF32Keys, D4 = D / 4;
+  constexpr int TILE4 = BC * D4;  // float4 per K or V tile
+  static_assert(TILE4 % 64 == 0, "tile must split evenly over a wave");
+  static_assert(NW * 2 * TILE4 * 4 >= NW * D * BR, "merge area must fit in the stages");
+  // Per wave: a K and a V stage.  After the key loop the same memory holds
+  // the waves' partial accumulators for the merge, [wave][column][row].
+  __shared__ float4 stage[NW][2][TILE4];
+  __shared__ float part_ml[NW][2][BR];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.S;
   const int BH = a.B * a.H;
   const int nq = (S + BR - 1) / BR;
@@ -37,7 +59,7 @@ __global__ __launch_bounds__(64, 1) void fa_fwd_f32_kernel(FwdArgs a) {
   int qt = blockIdx.x / BH;
   if (MASK != kMaskNone) qt = nq - 1 - qt;
   const int q0 = qt * BR;
-  const int row = q0 + tid;
+  const int row = q0 + lane;
   const size_t head_off = (size_t)bh * (size_t)S * D;   // q, o
   const size_t kv_off = (size_t)hp.kv * (size_t)S * D;  // k, v
   const float4 *qh = (const float4 *)((const float *)a.q + head_off);
@@ -61,36 +83,40 @@ __global__ __launch_bounds__(64, 1) void fa_fwd_f32_kernel(FwdArgs a) {
     if (MASK == kMaskWindow) kt_begin = max(0, q0 - a.window + 1) / BC;
   }
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
+  float4 *kl = &stage[wave][0][0], *vl = &stage[wave][1][0];
+  for (int kt = kt_begin + wave; kt < kt_end; kt += NW) {
     const int k0 = kt * BC;
-    __syncthreads();  // previous tile fully consumed
+    wave_lds_sync();  // this wave's previous tile fully read
 #pragma unroll
-    for (int i = 0; i < BC * D4 / 64; ++i) {
-      const int idx = tid + 64 * i;
+    for (int i = 0; i < TILE4 / 64; ++i) {
+      const int idx = lane + 64 * i;
       const int r = idx / D4;
       const bool in = k0 + r < S;
-      k_lds[idx] = in ? kh[(size_t)(k0 + r) * D4 + idx % D4] : make_float4(0.f, 0.f, 0.f, 0.f);
-      v_lds[idx] = in ? vh[(size_t)(k0 + r) * D4 + idx % D4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      kl[idx] = in ? kh[(size_t)(k0 + r) * D4 + idx % D4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      vl[idx] = in ? vh[(size_t)(k0 + r) * D4 + idx % D4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
+    wave_lds_sync();
 
+    // Scores of the 32 keys, accumulated key-interleaved (independent chains).
     float s[BC];
+#pragma unroll
+    for (int j = 0; j < BC; ++j) s[j] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D4; ++c)
+#pragma unroll
+      for (int j = 0; j < BC; ++j) {
+        const float4 kv = kl[j * D4 + c];
+        s[j] = fmaf(q[4 * c], kv.x, s[j]);
+        s[j] = fmaf(q[4 * c + 1], kv.y, s[j]);
+        s[j] = fmaf(q[4 * c + 2], kv.z, s[j]);
+        s[j] = fmaf(q[4 * c + 3], kv.w, s[j]);
+      }
     float tmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < BC; ++j) {
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < D4; ++c) {
-        const float4 kv = k_lds[j * D4 + c];
-        acc = fmaf(q[4 * c], kv.x, acc);
-        acc = fmaf(q[4 * c + 1], kv.y, acc);
-        acc = fmaf(q[4 * c + 2], kv.z, acc);
-        acc = fmaf(q[4 * c + 3], kv.w, acc);
-      }
-      float x = acc * a.scale_log2;
-      x = key_visible<MASK>(k0 + j, row, S, a.window) ? x : -INFINITY;
-      s[j] = x;
-      tmax = fmaxf(tmax, x);
+      const float x = s[j] * a.scale_log2;
+      s[j] = key_visible<MASK>(k0 + j, row, S, a.window) ? x : -INFINITY;
+      tmax = fmaxf(tmax, s[j]);
     }
     const float m_new = fmaxf(m, tmax);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -105,7 +131,7 @@ __global__ __launch_bounds__(64, 1) void fa_fwd_f32_kernel(FwdArgs a) {
       l += p;
 #pragma unroll
       for (int c = 0; c < D4; ++c) {
-        const float4 vv = v_lds[j * D4 + c];
+        const float4 vv = vl[j * D4 + c];
         o[4 * c] = fmaf(p, vv.x, o[4 * c]);
         o[4 * c + 1] = fmaf(p, vv.y, o[4 * c + 1]);
         o[4 * c + 2] = fmaf(p, vv.z, o[4 * c + 2]);
@@ -114,14 +140,46 @@ __global__ __launch_bounds__(64, 1) void fa_fwd_f32_kernel(FwdArgs a) {
     }
   }
 
-  if (row < S) {
-    const float inv = 1.f / l;
-    float4 *oh = (float4 *)((float *)a.o + head_off) + (size_t)row * D4;
+  // Merge the waves' partial states.  A wave that saw no visible key of a
+  // row has m = -inf, l = 0, O = 0 and gets factor 0.
+  __syncthreads();  // every wave is done with its stages
+  float *po = (float *)&stage[0][0][0];
 #pragma unroll
-    for (int c = 0; c < D4; ++c)
-      oh[c] = make_float4(o[4 * c] * inv, o[4 * c + 1] * inv, o[4 * c + 2] * inv,
-                          o[4 * c + 3] * inv);
-    a.lse[(size_t)bh * S + row] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+  for (int c = 0; c < D; ++c) po[(wave * D + c) * BR + lane] = o[c];
+  part_ml[wave][0][lane] = m;
+  part_ml[wave][1][lane] = l;
+  __syncthreads();
+  float mw[NW], m_tot = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mw[w] = part_ml[w][0][lane];
+    m_tot = fmaxf(m_tot, mw[w]);
+  }
+  float f[NW], l_tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    f[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - m_tot);
+    l_tot = fmaf(f[w], part_ml[w][1][lane], l_tot);
+  }
+  if (row < S) {
+    const float inv = 1.f / l_tot;
+    float *orow = (float *)a.o + head_off + (size_t)row * D;
+    constexpr int CPW = D / NW;  // output columns this wave merges
+#pragma unroll
+    for (int c4 = 0; c4 < CPW / 4; ++c4) {
+      float r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = wave * CPW + 4 * c4 + e;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc = fmaf(f[w], po[(w * D + c) * BR + lane], acc);
+        r[e] = acc * inv;
+      }
+      *(float4 *)(orow + wave * CPW + 4 * c4) = make_float4(r[0], r[1], r[2], r[3]);
+    }
+    if (wave == 0)
+      a.lse[(size_t)bh * S + row] = (m_tot + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
 }
 
@@ -129,16 +187,17 @@ template <int D, int MASK>
 bool run(const FwdArgs *a, hipStream_t stream, bool launch, LaunchInfo *info, hipError_t *err) {
   static char name[80];
   static const char *mk[3] = {"none", "causal", "window"};
-  snprintf(name, sizeof(name), "fa_fwd_f32<d%d,%s,br64,bc32>", D, mk[MASK]);
+  snprintf(name, sizeof(name), "fa_fwd_f32<d%d,%s,br64,bc32,w4>", D, mk[MASK]);
   info->name = name;
-  info->block_rows = 64;
-  info->threads = 64;
+  info->block_rows = kF32Rows;
+  info->threads = kF32Waves * 64;
   if (!launch) return true;
-  const int nq = (a->S + 63) / 64;
+  const int nq = (a->S + kF32Rows - 1) / kF32Rows;
   FwdArgs args = *a;
   void *kargs[] = {&args};
   *err = hipLaunchKernel((const void *)&fa_fwd_f32_kernel<D, MASK>,
-                         dim3((unsigned)(nq * a->B * a->H)), dim3(64), kargs, 0, stream);
+                         dim3((unsigned)(nq * a->B * a->H)), dim3(kF32Waves * 64), kargs, 0,
+                         stream);
   return true;
 }
 

@@ -155,7 +155,7 @@ def test_grid_full(dtype, d, mask, S):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mask", ["none", "causal", "window"])
-@pytest.mark.parametrize("S", [1, 77, 300])
+@pytest.mark.parametrize("S", [1, 77, 300, 1500])
 def test_f32_full(d, mask, S):
     window = 20 if mask == "window" else None
     q, k, v = make_inputs(2, 1, S, d, "f32", seed=S + d)
