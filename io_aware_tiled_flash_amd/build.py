@@ -29,7 +29,11 @@ SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_f32.hip", "fa_bwd_mfma.hip",
 #  * MFMA results (scores, output accumulators) are kept in VGPRs, where the
 #    softmax and the rescale use them, instead of AGPRs that would need a
 #    copy for every vector-ALU access.
-EXTRA_FLAGS = {"fa_fwd_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+#  The backward kernels use the VGPR-destination form too: their score and
+#  gradient blocks are read by the vector ALU every tile, and with AGPR
+#  results each read is a copy (a third of the dQ kernel's vector work).
+EXTRA_FLAGS = {"fa_fwd_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "fa_bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

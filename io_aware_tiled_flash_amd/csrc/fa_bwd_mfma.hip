@@ -347,14 +347,10 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
       if (HAS_PREV) {
         if (st + RPD < NS2) top[(st + RPD) % (RPD + 1)] = read_tr(st + RPD);
         const int kk = st / (2 * NDB), db = (st >> 1) % NDB;
-        // the gradient accumulators live in AGPRs: only MFMAs touch them
-        if (st & 1) {
+        if (st & 1)
           dkacc[db] = Ty::mfma(top[st % (RPD + 1)], dspk[kk], dkacc[db]);
-          asm volatile("" : "+a"(dkacc[db]));
-        } else {
+        else
           dvacc[db] = Ty::mfma(top[st % (RPD + 1)], ppk[par ^ 1][kk], dvacc[db]);
-          asm volatile("" : "+a"(dvacc[db]));
-        }
       }
       if (HAS_CUR) {
 #pragma unroll
@@ -428,10 +424,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 //
 // The same software pipeline as the dK/dV kernel, over the key tiles t the
 // work-group visits (each wave: its 32 rows against the tile's 32 keys):
-//   phase 1 of step t: S^T(t) = K_t Q^T and dP^T(t) = V_t dO^T on the matrix
-//     core, with dS^T(t-1) = P(t-1) * (dP^T(t-1) - D) and its packing beside;
-//   phase 2 of step t: dQ^T += K_{t-1}^T dS^T(t-1), with the weights of tile
-//     t, P = exp2(c S^T(t) - LSE log2 e), beside.
+//   phase 1 of step t: first the chain S^T(t) = K_t Q^T on the matrix core,
+//     with dS^T(t-1) = P(t-1) * (dP^T(t-1) - D) and its packing beside; then
+//     the chain dP^T(t) = V_t dO^T, with the weights of tile t,
+//     P = exp2(c S^T(t) - LSE log2 e), beside (S^T(t) is complete by then,
+//     and a dependent MFMA chain issues at the full rate);
+//   phase 2 of step t: dQ^T += K_{t-1}^T dS^T(t-1) on the matrix core.
+// This keeps the vector work of a tile beside the 16 MFMAs of phase 1 rather
+// than the 8 of phase 2.
 // Keys past the sequence read as zero rows: their dS^T column is multiplied
 // by a zero K row, so they need no mask; causal and window edges get a
 // fix-up on the tiles that straddle them.
@@ -543,10 +543,10 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
     const char *kc = (const char *)&k_lds[cur][0];
     const char *vc = (const char *)&v_lds[cur][0];
     const char *kp = (const char *)&k_lds[prev][0];
-    // ---- phase 1: S^T(u), dP^T(u) | dS^T(u-1) ----
+    // ---- phase 1: S^T(u) | dS^T(u-1), then dP^T(u) | weights of tile u ----
     u32x4 rop[RPD + 1];
     auto read_row = [&](int st) __attribute__((always_inline)) {
-      return off.row_op((st & 1) ? vc : kc, st >> 1);
+      return off.row_op(st >= NKS ? vc : kc, st % NKS);
     };
     if (HAS_CUR) {
 #pragma unroll
@@ -557,8 +557,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
     for (int st = 0; st < NS1; ++st) {
       if (HAS_CUR) {
         if (st + RPD < NS1) rop[(st + RPD) % (RPD + 1)] = read_row(st + RPD);
-        const int ks = st >> 1;
-        if (st & 1)
+        const int ks = st % NKS;
+        if (st >= NKS)
           dpacc[par] = Ty::mfma(rop[st % (RPD + 1)], doreg[ks], ks == 0 ? f32x16{} : dpacc[par]);
         else
           sacc = Ty::mfma(rop[st % (RPD + 1)], qreg[ks], ks == 0 ? f32x16{} : sacc);
@@ -566,9 +566,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int d = 0; d < LOADS; ++d)
         if ((d * NS1) / LOADS == st) dma(u + PF, ld, d);
-      if (HAS_PREV) {
+      if (HAS_PREV && st < NKS) {
 #pragma unroll
-        for (int r = st * 16 / NS1; r < (st + 1) * 16 / NS1; ++r) {
+        for (int r = st * 16 / NKS; r < (st + 1) * 16 / NKS; ++r) {
           const float v = pw[r] * (dpacc[par ^ 1][r] - drow);
           pw[r] = v;  // pw now holds dS^T(u-1)
           if (r & 1) {
@@ -577,9 +577,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
           }
         }
       }
+      if (HAS_CUR && st >= NKS) {
+        const int q = st - NKS;
+#pragma unroll
+        for (int r = q * 16 / NKS; r < (q + 1) * 16 / NKS; ++r) {
+          pw[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lse2));
+          pin(pw[r]);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- phase 2: dQ^T of tile u-1 | weights of tile u ----
+    // ---- phase 2: dQ^T of tile u-1 ----
     u32x4 top[RPD + 1];
     auto read_tr = [&](int st) __attribute__((always_inline)) {
       return off.tr_op(kp, st / NDB, st % NDB);
@@ -595,14 +603,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
         if (st + RPD < NS2) top[(st + RPD) % (RPD + 1)] = read_tr(st + RPD);
         const int kk = st / NDB, db = st % NDB;
         dqacc[db] = Ty::mfma(top[st % (RPD + 1)], dspk[kk], dqacc[db]);
-        asm volatile("" : "+a"(dqacc[db]));
-      }
-      if (HAS_CUR) {
-#pragma unroll
-        for (int r = st * 16 / NS2; r < (st + 1) * 16 / NS2; ++r) {
-          pw[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lse2));
-          pin(pw[r]);
-        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
