@@ -29,11 +29,13 @@ SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_f32.hip", "fa_bwd_mfma.hip",
 #  * MFMA results (scores, output accumulators) are kept in VGPRs, where the
 #    softmax and the rescale use them, instead of AGPRs that would need a
 #    copy for every vector-ALU access.
-#  The backward kernels use the VGPR-destination form too: their score and
-#  gradient blocks are read by the vector ALU every tile, and with AGPR
-#  results each read is a copy (a third of the dQ kernel's vector work).
+#  The backward and decode kernels use the VGPR-destination form too: their
+#  score blocks are read by the vector ALU every tile, and with AGPR results
+#  each read is a copy (a third of the dQ kernel's vector work; the decode
+#  matrix-core kernel ran at 2.9 TB/s that way and at 4.6 TB/s without).
 EXTRA_FLAGS = {"fa_fwd_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "fa_bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+               "fa_bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "fa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
