@@ -78,6 +78,17 @@ namespace {
 
 using namespace tile;
 
+// As load16_to_lds, for an LDS address that is already wave-uniform (a
+// scalar): no v_readfirstlane per load.
+__device__ inline void load16_to_lds_s(u32x4 rsrc, uint32_t byte_off, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(byte_off), "s"(rsrc)
+      : "memory");
+}
+
 // Offset-move cap: a lane's tile weight sum above it sends the wave to the
 // offset update.  bf16 weights share fp32's exponent range, so they may grow
 // to 2^32 before the offset has to move (the accumulator then stays below
@@ -88,7 +99,7 @@ template <> struct WeightCap<TBF16> { static constexpr float value = 4294967296.
 template <> struct WeightCap<TF16> { static constexpr float value = 256.0f; };
 
 #ifndef FA_RPD
-#define FA_RPD 3
+#define FA_RPD 2
 #endif
 
 template <class Ty, int D, int MASK, int NW, int BC, int NH, int PF>
@@ -178,6 +189,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // Direct loads of tile kt into K stage kst and V stage vst.  Chunk position
   // p of a stage holds row p / KCH, logical chunk c with swz(row, c) == p % KCH
   // (swz is an involution in c).
+  // LDS byte address of this wave's first 64-chunk block in stage 0 of K and
+  // of V: wave-uniform, so every direct load's LDS address is a scalar plus
+  // a compile-time offset.
+  const uint32_t k_lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)&k_lds[0][64 * wave * LOADS_PER_WAVE]);
+  const uint32_t v_lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)&v_lds[0][64 * wave * LOADS_PER_WAVE]);
+  constexpr uint32_t STAGE_BYTES = TILE_CHUNKS * 16;
   auto load_tile = [&](int kt, int kst, int vst) __attribute__((always_inline)) {
     const int k0 = kt * BC;
 #pragma unroll
@@ -186,8 +205,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       const int pos = 64 * blk + lane;
       const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
       const uint32_t off = (uint32_t)((k0 + r) * D + 8 * cc) * 2u;
-      load16_to_lds(rk, off, (uint32_t)(uintptr_t)&k_lds[kst][64 * blk]);
-      load16_to_lds(rv, off, (uint32_t)(uintptr_t)&v_lds[vst][64 * blk]);
+      load16_to_lds_s(rk, off, k_lds0 + kst * STAGE_BYTES + 1024u * i);
+      load16_to_lds_s(rv, off, v_lds0 + vst * STAGE_BYTES + 1024u * i);
     }
   };
 
@@ -450,9 +469,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
       const uint32_t off = (uint32_t)((lk0 + r) * D + 8 * cc) * 2u;
       if (d & 1)
-        load16_to_lds(rv, off, (uint32_t)(uintptr_t)&v_lds[lvs][64 * blk]);
+        load16_to_lds_s(rv, off, v_lds0 + lvs * STAGE_BYTES + 1024u * i);
       else
-        load16_to_lds(rk, off, (uint32_t)(uintptr_t)&k_lds[lks][64 * blk]);
+        load16_to_lds_s(rk, off, k_lds0 + lks * STAGE_BYTES + 1024u * i);
     };
     auto dma_slot = [](int d) constexpr { return 2 * d + 1; };
     static_assert(2 * NDMA <= MA, "direct loads must fit between the score MFMAs");
