@@ -292,19 +292,60 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     }
   };
 
-  // Elementwise mask of the raw scores (tiles straddling a band edge):
-  // invisible (query, key) pairs become -inf.
+  // Elementwise mask of the raw scores of a tile that straddles an edge of
+  // this wave's visible band or lies outside it: invisible (query, key)
+  // pairs become -inf.  The band test is made once per 32-row half (scalar
+  // branches): a half that sees none of the tile's keys is set to -inf
+  // outright, and a half that straddles an edge tests, per score, only the
+  // inequality of that edge (key <= row at the diagonal, key > row - window
+  // at a window's lower edge, key < S at the end of the sequence).
   auto apply_mask = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const int row = wr0 + 32 * h + lq;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (!key_visible<MASK>(key, row, S, a.window)) sacc[h][kb][r] = -INFINITY;
+      const int r0 = wr0 + 32 * h, r1 = r0 + 31;  // the half's rows
+      const int kl = k0 + BC - 1;                  // the tile's last key
+      bool none_visible, upper = false, lower = false, tail = false;
+      if (MASK == kMaskNone) {
+        none_visible = k0 >= S;
+        tail = kl >= S;
+      } else {
+        none_visible = k0 > r1;
+        upper = kl > r0;
+        if (MASK == kMaskWindow) {
+          none_visible = none_visible || kl <= r0 - a.window;
+          lower = k0 <= r1 - a.window;
         }
+      }
+      const int row = r0 + lq;
+      auto key_of = [&](int kb, int r) { return k0 + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3); };
+      if (none_visible) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[h][kb][r] = -INFINITY;
+        continue;
+      }
+      if (upper) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key_of(kb, r) > row) sacc[h][kb][r] = -INFINITY;
+      }
+      if (MASK == kMaskWindow && lower) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key_of(kb, r) <= row - a.window) sacc[h][kb][r] = -INFINITY;
+      }
+      if (MASK == kMaskNone && tail) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key_of(kb, r) >= S) sacc[h][kb][r] = -INFINITY;
+      }
     }
   };
 
