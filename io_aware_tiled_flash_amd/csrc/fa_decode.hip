@@ -44,7 +44,7 @@ constexpr int kMaxSplitLen = 4096;               // tokens per work-group at mos
 constexpr int kMaxTable = kMaxSplitLen + 2;      // table entries one split can touch
 constexpr float kTau = 8.f;                      // lazy-rescale threshold (base 2)
 #ifndef FA_DEC_MFMA_ROWS
-#define FA_DEC_MFMA_ROWS 8
+#define FA_DEC_MFMA_ROWS 5
 #endif
 constexpr int kMfmaRows = FA_DEC_MFMA_ROWS;      // query rows per key/value head for MFMA
 #ifndef FA_DEC_MFMA_GROUPS
@@ -666,8 +666,9 @@ bool decode_plan(int d, int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t 
   const int64_t rows_total = (H / Hkv) * n_q;
   // A key/value head serving many query rows goes to the matrix-core kernel
   // (16 rows per work-group); up to kMfmaRows - 1 rows stay on the vector
-  // ALUs.  Measured: at 4 rows the vector kernel is faster (5.7 against
-  // 5.3 TB/s), at 8 rows the matrix-core kernel (4.4 against 2.8 TB/s).  The vector kernel takes at most 4
+  // ALUs.  Measured: at 4 rows the vector kernel is faster (5.8 against
+  // 5.3 TB/s); at 5, 6 and 8 rows the matrix-core kernel (5.3 against 3.3,
+  // 5.3 against 3.4, 4.4 against 2.8 TB/s).  The vector kernel takes at most 4
   // rows per work-group: more rows slices (whose repeated cache reads hit
   // the shared L2) measured faster than 8-row work-groups, whose registers
   // cut the waves per SIMD from 5 to 3.

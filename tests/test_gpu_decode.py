@@ -1,6 +1,6 @@
 """GPU parity of paged-cache decoding: the HIP kernels against the fp64
 oracle (oracle/decode.py) on identical seeded inputs.  Key/value heads that
-serve up to 7 query rows run on the vector-ALU kernel, 8 or more on the
+serve up to 4 query rows run on the vector-ALU kernel, 5 or more on the
 matrix-core kernel; the cases cover both, with and without split contexts.
 
 Bars: the attention output bars, max |O_gpu - O_oracle| <= 2e-2 for bf16 and
@@ -98,7 +98,9 @@ CASES = [
     ("bf16", 128, 2, 16, 2, 2, 16, (3000, 40)),      # 16 rows, split context (matrix core)
     ("f16", 64, 3, 12, 1, 1, 16, (1, 129, 2500)),    # 12 rows (matrix core)
     ("bf16", 128, 2, 40, 4, 1, 16, (900, 5000)),     # 10 rows (matrix core)
-    ("bf16", 128, 2, 28, 4, 1, 16, (900, 5000)),     # 7 rows: vector, 2 slices of 4
+    ("bf16", 128, 2, 28, 4, 1, 16, (900, 5000)),     # 7 rows (matrix core)
+    ("bf16", 128, 2, 20, 4, 1, 16, (900, 5000)),     # 5 rows (matrix core)
+    ("f16", 128, 2, 16, 4, 1, 16, (700, 4500)),      # 4 rows: vector
     ("f16", 64, 2, 16, 2, 1, 16, (3, 2100)),         # 8 rows (matrix core)
 ]
 
