@@ -3,11 +3,13 @@
  * backward passes).
  *
  * The operation is exact attention O = softmax(scale * Q K^T) V evaluated tile
- * by tile with the online softmax: a running row maximum m, a running
- * denominator l, rescaling of an unnormalised output accumulator by
- * exp(m_old - m_new) whenever the maximum grows, and a single division by l at
- * the end, so that no score or probability matrix is ever written to device
- * memory.  The method is the one described in "FlashAttention: Why Tiling
+ * by tile with the online softmax: a running row offset m (the running
+ * maximum's role), a running denominator l, rescaling of an unnormalised
+ * output accumulator by exp(m_old - m_new) when m moves, and a single division
+ * by l at the end, so that no score or probability matrix is ever written to
+ * device memory.  (The bf16/fp16 forward kernels move m only when a tile's
+ * weights would grow past a fixed bound, which gives the same result up to
+ * rounding.)  The method is the one described in "FlashAttention: Why Tiling
  * Attention Makes Transformers Fast Without Changing the Result" (Dev.to),
  * sections "Online softmax: correct as you go" and "The tiled forward pass",
  * and in the aicomputerinstitute.com grade-12 chapter on flash attention,
