@@ -221,11 +221,8 @@ def bench_decode(args) -> int:
                    "d": w.d, "block_size": w.block_size, "ctx": [w.ctx_lo, w.ctx_hi],
                    "cached_tokens": int(c.sum()), "pass": "decode",
                    "splits": "none" if ws_bytes == 0 else "split + merge",
-                   # label only: the library sends 8 or more query rows per
-                   # key/value head to its matrix-core kernel
-                   "kernel": "fa_decode_paged (" + ("vector-ALU" if w.H // w.Hkv * w.n_q < 8
-                                                     else "matrix-core")
-                             + " kernel" + ("" if ws_bytes == 0 else " + merge kernel") + ")"},
+                   "rows_per_kv_head": w.H // w.Hkv * w.n_q,
+                   "kernel": "fa_decode_paged" + ("" if ws_bytes == 0 else " + merge")},
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
