@@ -49,6 +49,15 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
  */
 typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW = 2 } fa_mask;
 
+/*
+ * Status of every call.  A valid request that no kernel serves is an error
+ * (FA_EUNSUPPORTED), never a quiet switch to a slower path: the
+ * foundry.adhana.ai page, section "Failure modes", names the silent fallback
+ * to unfused attention as the usual way the method's benefit is lost without
+ * notice, and the Dev.to article's section "Using it in practice" warns that
+ * the fast path is taken only when its conditions (dtype, head size, mask)
+ * hold.
+ */
 typedef enum {
   FA_OK = 0,
   FA_EINVAL = 1,        /* an argument is invalid (see fa_fwd)                     */
@@ -85,13 +94,17 @@ typedef enum {
  * without a GPU; nothing is launched when one is returned):
  *   FA_EINVAL      null pointer; a pointer not 16-byte aligned; B, H, S or d
  *                  < 1; unknown dtype or mask; window < 1 with
- *                  FA_MASK_WINDOW; non-finite scale; o overlapping q, k, v or
+ *                  FA_MASK_WINDOW; a scale that is not finite or whose
+ *                  product with log2(e) overflows fp32 (|scale| above about
+ *                  2.4e38: the kernels work in base 2); o overlapping q, k, v or
  *                  lse, or lse overlapping q, k or v; a size whose byte count
  *                  overflows, or a single head larger than 2 GiB.
  *   FA_EUNSUPPORTED (dtype, d) without a kernel.
  *   FA_EHIP        the launch failed; fa_last_error() holds the HIP message.
  * With the environment variable FA_LOG=1 each call prints the chosen kernel
- * and grid to stderr.
+ * and grid to stderr: the foundry.adhana.ai page, section "Evals", asks that
+ * the backend actually selected be logged on every run, so that a measurement
+ * can be tied to the kernel that produced it.
  */
 fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                  int64_t B, int64_t H, int64_t S, int64_t d, int dtype, int mask,
@@ -154,7 +167,7 @@ fa_status fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float
  * Errors, all checked on the host before any launch:
  *   FA_EINVAL       a null or not 16-byte-aligned pointer; B, H, Hkv, S or d
  *                   < 1; Hkv not dividing H; unknown dtype or mask; window <
- *                   1 with FA_MASK_WINDOW; non-finite scale; any of dq, dk,
+ *                   1 with FA_MASK_WINDOW; a scale rejected as by fa_fwd; any of dq, dk,
  *                   dv, delta overlapping an input or another of them; byte
  *                   counts that overflow, or one head larger than 2 GiB.
  *   FA_EUNSUPPORTED FA_F32, or d outside {64, 128}.
@@ -209,7 +222,7 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
  *                   o or workspace not 16-byte aligned, block_table, ctx_lens
  *                   or lse not 4-byte aligned; B, H, Hkv, n_q, d, num_blocks,
  *                   block_size or max_blocks < 1; max_ctx < 0; Hkv not
- *                   dividing H; unknown dtype; non-finite scale; workspace
+ *                   dividing H; unknown dtype; a scale rejected as by fa_fwd; workspace
  *                   smaller than required; o, lse or workspace overlapping an
  *                   input or each other; sizes beyond the kernels' index range.
  *   FA_EUNSUPPORTED FA_F32, d outside {64, 128}, or a block_size that is not a
@@ -240,17 +253,32 @@ fa_status fa_decode_workspace_size(int64_t B, int64_t H, int64_t Hkv, int64_t n_
  * NUL-terminated name into kernel_name[0..len) (truncated if needed; may be
  * NULL when len == 0).  Returns FA_OK, FA_EINVAL (bad enum or d < 1) or
  * FA_EUNSUPPORTED (no kernel for that combination).
+ * Purpose: the Dev.to article's section "Using it in practice" tells the
+ * user to verify which attention implementation is dispatched rather than
+ * assume the fast one runs; the foundry.adhana.ai page's "Evals" section
+ * makes the same check part of every evaluation.  This call answers that
+ * question before any launch.
  */
 fa_status fa_query(int64_t d, int dtype, int mask, char *kernel_name, size_t len);
 
-/* Static English text for a status code (never NULL). */
+/*
+ * fa_status_str -- static English text for a status code (never NULL).
+ * fa_last_error -- detail of the last non-OK status returned on the calling
+ * thread ("" if none), e.g. which (dtype, head size) has no kernel; the
+ * string stays valid until the next fa_* call on that thread.
+ * Both exist so that an unsupported or invalid request fails loudly and says
+ * why, which is what the foundry.adhana.ai page ("Failure modes") asks of a
+ * fused-attention path instead of a silent fallback.
+ */
 const char *fa_status_str(int status);
-
-/* Detail of the last non-OK status returned on the calling thread ("" if
- * none).  The string stays valid until the next fa_* call on that thread. */
 const char *fa_last_error(void);
 
-/* FA_ABI_VERSION of the loaded library. */
+/*
+ * fa_abi_version -- FA_ABI_VERSION of the loaded library.  A binding checks
+ * it before its first call, so that a stale library is an error rather than
+ * a different kernel running unnoticed (the same "verify the dispatch" check
+ * as fa_query, Dev.to "Using it in practice").
+ */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -2,9 +2,9 @@
 ``libfa.so``.
 
 The functions ``fa_fwd``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_decode_paged``,
-``fa_decode_workspace_size``, ``fa_query``, ``fa_status_str``,
-``fa_last_error`` and ``fa_abi_version`` mirror the C ABI declared in
-``include/fa.h`` one to one (argument marshalling only).  ``forward``,
+``fa_decode_workspace_size``, ``fa_query``,
+``fa_status_str``, ``fa_last_error`` and ``fa_abi_version`` mirror the C ABI
+declared in ``include/fa.h`` one to one (argument marshalling only).  ``forward``,
 ``backward`` and ``decode`` are the tensor-level convenience wrappers: they
 check the tensors, allocate the outputs with torch and launch on torch's
 current stream.  Every arithmetic step runs in the HIP
@@ -18,8 +18,8 @@ import math
 import os
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_decode_paged",
-           "fa_decode_workspace_size", "fa_query", "fa_status_str", "fa_last_error",
-           "fa_abi_version", "forward", "backward", "decode", "library_path", "DTYPES", "MASKS",
+           "fa_decode_workspace_size",
+           "fa_query", "fa_status_str", "fa_last_error", "fa_abi_version", "forward", "backward", "decode", "library_path", "DTYPES", "MASKS",
            "FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
 
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
@@ -200,6 +200,11 @@ def forward(q, k, v, mask: str = "none", window: int | None = None,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    # A host tensor would pass every check of the C library (which cannot
+    # tell host from device pointers) and fault in the kernel's stores.
+    for name, t in (("out", out), ("lse", lse)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != q.device:
+            raise FaError(FA_EINVAL, f"{name} must be a device tensor on q's device")
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise FaError(FA_EINVAL, "out must match q")
     if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():

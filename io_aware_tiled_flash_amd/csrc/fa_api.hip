@@ -43,6 +43,14 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
 
+// The kernels work in base 2 on scale * log2(e), rounded to fp32: a finite
+// scale above about 2.4e38 would turn that factor into inf, and inf times a
+// zero score into NaN.
+constexpr double kLog2e = 1.4426950408889634;
+bool scale_ok(float scale) {
+  return isfinite(scale) && isfinite((float)((double)scale * kLog2e));
+}
+
 // Resolve (dtype, d, mask) to a kernel; `launch` false only fills `info`.
 bool dispatch(int dtype, int d, int mask, const fa::FwdArgs *a, hipStream_t stream, bool launch,
               fa::LaunchInfo *info, hipError_t *err) {
@@ -79,7 +87,9 @@ fa_status fwd_impl(const char *name, const void *q, const void *k, const void *v
   if (mask == FA_MASK_WINDOW && window < 1)
     return fail(FA_EINVAL, "window must be >= 1 for the sliding-window mask (got %lld)",
                 (long long)window);
-  if (!isfinite(scale)) return fail(FA_EINVAL, "scale must be finite");
+  if (!scale_ok(scale))
+    return fail(FA_EINVAL, "scale must be finite, with scale*log2(e) finite in fp32 (got %g)",
+                (double)scale);
 
   const int64_t esz = dtype == FA_F32 ? 4 : 2;
   int64_t bh, rows, elems, bytes, row_bytes, head_bytes, lse_bytes, bhkv, kv_bytes;
@@ -115,7 +125,7 @@ fa_status fwd_impl(const char *name, const void *q, const void *k, const void *v
   a.Hkv = (int)Hkv;
   a.S = (int)S;
   a.window = eff_mask == FA_MASK_WINDOW ? (int)window : 0;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = (float)((double)scale * kLog2e);
 
   fa::LaunchInfo info = {nullptr, 0, 0};
   hipError_t err = hipSuccess;
@@ -162,7 +172,9 @@ fa_status bwd_impl(const void *q, const void *k, const void *v, const void *o, c
   if (mask == FA_MASK_WINDOW && window < 1)
     return fail(FA_EINVAL, "window must be >= 1 for the sliding-window mask (got %lld)",
                 (long long)window);
-  if (!isfinite(scale)) return fail(FA_EINVAL, "scale must be finite");
+  if (!scale_ok(scale))
+    return fail(FA_EINVAL, "scale must be finite, with scale*log2(e) finite in fp32 (got %g)",
+                (double)scale);
 
   const int64_t esz = dtype == FA_F32 ? 4 : 2;
   int64_t bh, rows, elems, bytes, row_bytes, head_bytes, stat_bytes, bhkv, kv_bytes;
@@ -210,7 +222,7 @@ fa_status bwd_impl(const void *q, const void *k, const void *v, const void *o, c
   a.S = (int)S;
   a.window = eff_mask == FA_MASK_WINDOW ? (int)window : 0;
   a.scale = scale;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = (float)((double)scale * kLog2e);
 
   fa::LaunchInfo info = {nullptr, 0, 0};
   hipError_t err = hipSuccess;
@@ -292,7 +304,9 @@ fa_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
     if ((uintptr_t)need4[i] % 4 != 0)
       return fail(FA_EINVAL, "block_table, ctx_lens and lse must be 4-byte aligned");
   }
-  if (!isfinite(scale)) return fail(FA_EINVAL, "scale must be finite");
+  if (!scale_ok(scale))
+    return fail(FA_EINVAL, "scale must be finite, with scale*log2(e) finite in fp32 (got %g)",
+                (double)scale);
   int sh = 0;
   int64_t cap = 0;
   fa::DecodePlan plan;
@@ -348,7 +362,7 @@ fa_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
   a.n_splits = plan.n_splits;
   a.rows = plan.rows;
   a.row_slices = plan.row_slices;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = (float)((double)scale * kLog2e);
 
   fa::LaunchInfo info = {nullptr, 0, 0};
   hipError_t err = hipSuccess;

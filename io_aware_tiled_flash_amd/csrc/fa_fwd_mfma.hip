@@ -78,8 +78,8 @@ namespace {
 
 using namespace tile;
 
-// As load16_to_lds, for an LDS address that is already wave-uniform (a
-// scalar): no v_readfirstlane per load.
+// As load16_to_lds (M0 handling included), for an LDS address that is
+// already wave-uniform (a scalar): no v_readfirstlane per load.
 __device__ inline void load16_to_lds_s(u32x4 rsrc, uint32_t byte_off, uint32_t lds_addr) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"

@@ -80,13 +80,18 @@ __device__ inline u32x4 rsrc_words(const void *base, uint32_t bytes) {
 // outstanding direct load before each LDS read and each barrier, which
 // serialises the multi-tile prefetch.  Completion is awaited explicitly with
 // s_waitcnt vmcnt (vector-memory loads complete in issue order).
+// M0 (the LDS base of the direct loads) is a reserved register for this
+// compiler: it allocates no value to it, and a clobber list naming it is
+// ignored (the compiler warns as much), so none is given.  The kernels rely
+// on no compiler-generated instruction reading M0; tests/test_isa.py checks
+// that in the generated code.
 __device__ inline void load16_to_lds(u32x4 rsrc, uint32_t byte_off, uint32_t lds_addr) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "buffer_load_dwordx4 %1, %2, 0 offen lds"
       :
       : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(byte_off), "s"(rsrc)
-      : "memory");  // M0 is only ever set by these statements in this kernel
+      : "memory");
 }
 
 // 4 bytes per lane from global memory straight into LDS (lane i's bytes land

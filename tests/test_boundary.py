@@ -91,6 +91,7 @@ def _call(**kw):
     (dict(dtype=3), "dtype"), (dict(dtype=-1), "dtype"), (dict(mask=3), "mask"),
     (dict(mask=2, window=0), "window"), (dict(mask=2, window=-5), "window"),
     (dict(scale=float("nan")), "finite"), (dict(scale=float("inf")), "finite"),
+    (dict(scale=3e38), "finite"), (dict(scale=-2.5e38), "finite"),
     (dict(o=A + 16), "overlap"), (dict(o=A + 128 * MB + 32 * 1024), "overlap"),
     (dict(lse=A + 64 * MB + 1024), "overlap"), (dict(o=A + 256 * MB - 16), "overlap"),
     (dict(B=1 << 40, H=1 << 30), "overflow"), (dict(S=1 << 24, d=256), "2 GiB"),
@@ -160,6 +161,7 @@ def _call_bwd(**kw):
     (dict(B=0), "sizes"), (dict(Hkv=0), "sizes"), (dict(S=0), "sizes"), (dict(d=-1), "sizes"),
     (dict(Hkv=3), "divide"), (dict(dtype=5), "dtype"), (dict(mask=-1), "mask"),
     (dict(mask=2, window=0), "window"), (dict(scale=float("nan")), "finite"),
+    (dict(scale=3e38), "finite"),
     (dict(dq=A + 16), "dq overlaps an input"),              # inside q
     (dict(dk=A + 80 * MB + 64 * 1024), "dk overlaps"),      # inside dout
     (dict(delta=A + 64 * MB + 1024), "delta overlaps"),     # inside lse
@@ -225,6 +227,7 @@ def _ws(**kw):
     (dict(B=0), "sizes"), (dict(n_q=0), "sizes"), (dict(num_blocks=0), "sizes"),
     (dict(block_size=0), "sizes"), (dict(max_blocks=0), "sizes"), (dict(max_ctx=-1), "max_ctx"),
     (dict(Hkv=3), "divide"), (dict(dtype=7), "dtype"), (dict(scale=float("inf")), "finite"),
+    (dict(scale=-3e38), "finite"),
     (dict(o=A + 16 * MB + 4096), "o overlaps"),                 # inside k_cache
     (dict(lse=A + 112 * MB + 64), "lse overlaps"),              # inside block_table
     (dict(o=A + 115 * MB - 16), "o and lse overlap"),
@@ -276,6 +279,14 @@ def test_decode_refuses_host_tensors():
         fa.decode(q, kc, kc, torch.zeros(1, 2, dtype=torch.int32),
                   torch.ones(1, dtype=torch.int32), max_ctx=32)
     assert e.value.status == fa.FA_EINVAL
+
+
+def test_largest_scales_whose_base2_factor_is_finite_are_accepted():
+    # 2.3e38 * log2(e) = 3.32e38 < FLT_MAX: valid, so the call reaches
+    # dispatch (an unsupported d keeps anything from launching).
+    assert _call(scale=2.3e38, d=96) == fa.FA_EUNSUPPORTED
+    assert _call(scale=-2.3e38, d=96) == fa.FA_EUNSUPPORTED
+    assert _call_bwd(scale=2.3e38, d=96) == fa.FA_EUNSUPPORTED
 
 
 def test_window_argument_ignored_without_window_mask():

@@ -158,19 +158,14 @@ def test_backward_outputs_do_not_touch_neighbours():
         assert torch.equal(b[pad:pad + n].view_as(r), r)
 
 
-@pytest.mark.parametrize("name", ["prefill_8k_d128"])
-def test_backward_full_size_workload(name):
-    """The benchmark's backward configuration at full size.  Every head:
-    sum_j dV[j] = sum_i dO[i] (each row's probabilities sum to one), within
-    the sum of the per-element bounds, which for this identity needs only dO
-    and dV.  Two whole heads: every element against the oracle within its
-    bound."""
-    from bwd_bounds import UNIT, F32, head_bounds
-    from oracle import attention_bwd_rows_ref
+@pytest.fixture(scope="module")
+def full_size_backward():
+    """The benchmark's backward configuration at full size, run once on the
+    GPU for the tests below (inputs and gradients on the host)."""
     from workloads import WORKLOADS
 
-    w = WORKLOADS[name]
-    _say(f"bwd full-size {name}")
+    w = WORKLOADS["prefill_8k_d128"]
+    _say(f"bwd full-size {w.name}: launching")
     q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers, w.kv_heads)
     do = make_grad(w.B, w.H, w.S, w.d, w.dtype, w.seed + 7919)
     dev = torch.device("cuda:0")
@@ -179,10 +174,18 @@ def test_backward_full_size_workload(name):
     dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, mask=w.mask, window=w.window or None,
                              scale=w.scale)
     torch.cuda.synchronize()
-    dq, dk, dv, lse = dq.cpu(), dk.cpu(), dv.cpu(), lse.cpu()
+    return w, (q, k, v, do), (dq.cpu(), dk.cpu(), dv.cpu()), lse.cpu()
+
+
+def test_backward_full_size_identity(full_size_backward):
+    """Every head: sum_j dV[j] = sum_i dO[i] (each row's probabilities sum to
+    one), within the sum of the per-element bounds, which for this identity
+    needs only dO and dV."""
+    from bwd_bounds import UNIT, F32
+
+    w, (q, k, v, do), (dq, dk, dv), lse = full_size_backward
     for name_, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.isfinite(t.float()).all(), f"{name_} not finite"
-
     u = UNIT[w.dtype]
     g = (w.S + w.d + 16) * F32
     group = w.H // w.kv_heads
@@ -200,15 +203,39 @@ def test_backward_full_size_workload(name):
             gap = ((lhs - rhs).abs() / tol).max().item()
             assert gap <= 1.0, f"kv head {gh}: sum_j dV - sum_i dO reaches {gap:.3f} of bound"
 
-    assert w.kv_heads == w.H, "the whole-head check below assumes one query head per kv head"
-    for h in (0, w.H - 1):
-        _say(f"  head {h}: exact gradients and bounds")
+
+@pytest.mark.parametrize("first", [0, 8, 16, 24])
+def test_backward_full_size_every_element(full_size_backward, first):
+    """Heads first .. first+7 of the full-size backward: every element of dQ,
+    dK and dV against the oracle's exact gradients, within its bound.  The
+    heads run on a thread pool (the oracle's numpy work releases the GIL)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from bwd_bounds import UNIT, head_bounds
+    from oracle import attention_bwd_rows_ref
+
+    w, (q, k, v, do), (dq, dk, dv), _ = full_size_backward
+    assert w.kv_heads == w.H, "the whole-head check assumes one query head per kv head"
+    u = UNIT[w.dtype]
+
+    def one(h):
         args = (q[0, h], k[0, h], v[0, h], do[0, h], w.mask, w.window or None, w.scale)
         ref = attention_bwd_rows_ref(*args)
         bnd = head_bounds(*args, w.dtype)
-        for name_, got, r, e in zip(("dq", "dk", "dv"), (dq[0, h], dk[0, h], dv[0, h]), ref,
-                                    bnd):
-            b_ = e + u * np.abs(r)
-            x = excess(got, r, b_)
-            _say(f"  head {h} {name_}: {x:.3f} of bound")
+        out = []
+        for got, r, e in zip((dq[0, h], dk[0, h], dv[0, h]), ref, bnd):
+            out.append(excess(got, r, e + u * np.abs(r)))
+        return out
+
+    heads = list(range(first, min(first + 8, w.H)))
+    _say(f"bwd full-size: heads {heads[0]}..{heads[-1]}, exact gradients and bounds")
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with threadpool_limits(limits=2), ThreadPoolExecutor(workers) as ex:
+        res = list(ex.map(one, heads))
+    for h, xs in zip(heads, res):
+        _say(f"  head {h}: dq {xs[0]:.3f}, dk {xs[1]:.3f}, dv {xs[2]:.3f} of bound")
+        for name_, x in zip(("dq", "dk", "dv"), xs):
             assert x <= 1.0, f"head {h}: {name_} error reaches {x:.3f} of its bound"

@@ -1,13 +1,16 @@
 """GPU parity: the HIP kernels against the fp64 oracle on identical seeded inputs.
 
 Bars (stated for this path): max |O_gpu - O_oracle| <= 2e-2 for bf16 inputs,
-5e-3 for fp16, 1e-5 for fp32; max |LSE_gpu - LSE_oracle| <= 1e-3.  Small shapes
-are compared element by element in full; the full-size workloads, launched
-exactly as the benchmark launches them, are compared on sampled rows the
-oracle computes one by one, plus properties that hold at any size.
+5e-3 for fp16, 1e-5 for fp32; max |LSE_gpu - LSE_oracle| <= 1e-3.  Every
+shape, the full-size workloads included (launched exactly as the benchmark
+launches them), is compared element by element against the oracle over all
+rows of all heads.  The full-size workloads also get a fast pre-check on
+sampled rows and properties that hold at any size.
 """
 import math
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -77,6 +80,41 @@ def _check_sampled(q, k, v, o, lse, mask, window, scale, dtype, label, n_rows=48
     assert worst_l <= LSE_TOL, f"{label}: sampled max|dLSE| = {worst_l}"
 
 
+def _oracle_workers():
+    # the oracle's elementwise numpy work releases the GIL on large arrays, so
+    # a thread pool spreads the chunks over the host's cores (16 at most: the
+    # share of one GPU's host)
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _check_all_rows(q, k, v, o, lse, mask, window, scale, dtype, label, row_chunk=2048):
+    """Every row of every head against the oracle, chunk by chunk (each
+    chunk's scores and probabilities materialised in fp64, as attention_ref
+    does), without holding the whole fp64 result."""
+    from threadpoolctl import threadpool_limits
+
+    B, H, S, d = q.shape
+    group = H // k.shape[1]
+    jobs = [(b, h, r0) for b in range(B) for h in range(H) for r0 in range(0, S, row_chunk)]
+
+    def one(job):
+        b, h, r0 = job
+        rows = np.arange(r0, min(S, r0 + row_chunk))
+        g = h // group
+        o_ref, lse_ref = attention_rows_ref(q[b, h], k[b, g], v[b, g], rows, mask, window, scale)
+        eo = float(np.abs(o[b, h, rows].double().numpy() - o_ref).max())
+        el = float(np.abs(lse[b, h, rows].double().numpy() - lse_ref).max())
+        return eo, el
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(_oracle_workers()) as ex:
+        res = list(ex.map(one, jobs))
+    worst_o = max(r[0] for r in res)
+    worst_l = max(r[1] for r in res)
+    _say(f"{label}: all {B * H * S} rows, max|dO| = {worst_o:.3e}, max|dLSE| = {worst_l:.3e}")
+    assert worst_o <= O_TOL[dtype], f"{label}: max|dO| = {worst_o}"
+    assert worst_l <= LSE_TOL, f"{label}: max|dLSE| = {worst_l}"
+
+
 # --------------------------------------------------------------------------
 # the pages' worked example, through the kernel
 # --------------------------------------------------------------------------
@@ -136,6 +174,20 @@ def test_large_workloads_sampled(name):
     _check_sampled(q, k, v, o, lse, w.mask, w.window or None, w.scale, w.dtype, name)
 
 
+@pytest.mark.parametrize("name", ["prefill_8k_d128", "window_18k_d128", "full_d256_f16",
+                                  "prefill_8k_d128_gqa4"])
+def test_large_workloads_every_row(name):
+    """The full-size workloads, every output element and every logsumexp
+    against the oracle."""
+    w = WORKLOADS[name]
+    _say(f"{name}: generating inputs")
+    q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers, w.kv_heads)
+    _say(f"{name}: launching")
+    o, lse = _run(q, k, v, w.mask, w.window or None, w.scale)
+    _say(f"{name}: oracle over every row ({_oracle_workers()} threads)")
+    _check_all_rows(q, k, v, o, lse, w.mask, w.window or None, w.scale, w.dtype, name)
+
+
 # --------------------------------------------------------------------------
 # shapes, masks, ragged tails
 # --------------------------------------------------------------------------
@@ -178,6 +230,29 @@ def test_many_heads_small_sequence():
 def test_scale_values(scale):
     q, k, v = make_inputs(1, 2, 300, 128, "f16", seed=11)
     _check_full(q, k, v, "causal", None, scale, "f16", f"scale={scale}")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f32", 64)])
+@pytest.mark.parametrize("mask", ["none", "causal", "window"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0])
+def test_negative_and_zero_scale(dtype, d, mask, scale):
+    """A negative scale (the matrix-core kernels flip Q's sign bits) and a
+    zero scale (run as a vanishing positive one): against the oracle, and
+    for scale 0 against the closed form, O = the mean of the visible V rows
+    and LSE = ln(number of visible keys)."""
+    S, window = 300, (41 if mask == "window" else None)
+    q, k, v = make_inputs(1, 2, S, d, dtype, seed=17 + d)
+    o, lse = _check_full(q, k, v, mask, window, scale, dtype,
+                         f"scale={scale} {dtype} d={d} {mask}")
+    if scale == 0.0:
+        i = np.arange(S)
+        lo = np.zeros(S, dtype=np.int64) if mask != "window" else np.maximum(0, i - window + 1)
+        hi = np.full(S, S) if mask == "none" else i + 1
+        csum = np.concatenate([np.zeros((1, 2, 1, d)), np.cumsum(v.double().numpy(), axis=2)],
+                              axis=2)
+        mean = (csum[:, :, hi] - csum[:, :, lo]) / (hi - lo)[None, None, :, None]
+        assert np.abs(o.double().numpy() - mean).max() <= O_TOL[dtype]
+        assert np.abs(lse.double().numpy() - np.log(hi - lo)).max() <= LSE_TOL
 
 
 @pytest.mark.parametrize("dtype,jump", [("bf16", 26.0), ("f16", 7.0)])
@@ -264,6 +339,30 @@ def test_outputs_do_not_touch_neighbours():
     torch.cuda.synchronize()
     assert bool((big[:q.numel()] == 7.0).all()) and bool((big[2 * q.numel():] == 7.0).all())
     assert bool((lbig[:260] == 9.0).all()) and bool((lbig[520:] == 9.0).all())
+
+
+def test_forward_refuses_host_outputs(monkeypatch):
+    """out and lse must be device tensors on q's device: a host buffer would
+    pass the library's pointer checks and fault in the kernel's stores.  The
+    launch entry points are replaced by stubs that fail the test if called,
+    so no kernel can run even if the check regressed."""
+    def boom(*a, **kw):
+        raise AssertionError("a kernel was launched with a host output buffer")
+
+    monkeypatch.setattr(fa, "fa_fwd", boom)
+    monkeypatch.setattr(fa, "fa_fwd_gqa", boom)
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device=dev)
+    kg = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device=dev)
+    o_host = torch.empty(1, 2, 64, 64, dtype=torch.bfloat16)
+    l_host = torch.empty(1, 2, 64)
+    o_dev = torch.empty_like(q)
+    l_dev = torch.empty(1, 2, 64, device=dev)
+    for kk in (q, kg):  # plain and grouped heads
+        for out, lse in ((o_host, l_dev), (o_dev, l_host), (o_host, l_host)):
+            with pytest.raises(fa.FaError) as e:
+                fa.forward(q, kk, kk, mask="causal", out=out, lse=lse)
+            assert e.value.status == fa.FA_EINVAL and "device" in str(e.value)
 
 
 # --------------------------------------------------------------------------

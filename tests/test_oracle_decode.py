@@ -215,6 +215,36 @@ def test_grouped_heads_equal_repeated_heads():
 
 # -- table entries that hold no block, context lengths out of range ---------------
 
+def test_shared_prefix_blocks_equal_private_copies():
+    """Copy-on-write prefix sharing (aicomputerinstitute.com flash-attention
+    chapter, "PagedAttention: memory management borrowed from an operating
+    system"): several requests whose tables name the same physical blocks for
+    a common prefix give exactly what they give with that prefix copied into
+    blocks of their own, and a request sharing another's whole context (and
+    query) reproduces that request's result."""
+    q, kc, vc, table, ctx = make_decode_inputs(3, 4, 2, 1, 16, "bf16", 4, 5,
+                                               ctx_lens=[30, 41, 30], extra_blocks=2)
+    P = 5
+    shared = table.clone()
+    kc_own, vc_own = kc.clone(), vc.clone()
+    for b in (1, 2):
+        shared[b, :P] = table[0, :P]
+        kc_own[table[b, :P].long()] = kc[table[0, :P].long()]
+        vc_own[table[b, :P].long()] = vc[table[0, :P].long()]
+    o_s, l_s = paged_decode_ref(q, kc, vc, shared, ctx)
+    o_c, l_c = paged_decode_ref(q, kc_own, vc_own, table, ctx)
+    assert np.array_equal(o_s, o_c) and np.array_equal(l_s, l_c)
+    # request 2 shares all of request 0's blocks and its query: same result
+    full = table.clone()
+    full[2] = table[0]
+    q2 = q.clone()
+    q2[2] = q[0]
+    o_f, l_f = paged_decode_ref(q2, kc, vc, full, ctx)
+    assert np.array_equal(o_f[2], o_f[0]) and np.array_equal(l_f[2], l_f[0])
+    # and sharing did change what request 1 sees (the prefix is not its own)
+    assert not np.allclose(o_s[1], paged_decode_ref(q, kc, vc, table, ctx)[0][1])
+
+
 def test_invalid_entries_hold_no_tokens():
     q, kc, vc, table, ctx = _inputs(ctx=(9, 6, 13), n_q=1, bs=4)
     nb = kc.shape[0]
