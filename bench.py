@@ -4,11 +4,18 @@ One step is one ``fa_fwd`` launch over the whole batch of the workload (all
 of the hot path: tile loads, QK^T, masking, online softmax, PV, epilogue).
 With ``--pass bwd`` a step is one ``fa_bwd`` call instead (gradients of the
 same workload, given the forward's outputs and a seeded output gradient).
-Inputs are generated once, copied to HBM and reused; W untimed steps, then K
-steps timed with events on the launch stream, bracketed by synchronisation.
-The default W is about a second of work: under sustained MFMA load the
-MI355X clock takes on the order of a second to settle, and a few warm-up
-steps alone report it cold (about a quarter slower).
+Inputs are generated once, copied to HBM and reused.  Before the W untimed
+warm-up steps a clock-settling phase repeats the step for ``--settle-s``
+seconds (default 1; 0 disables it): under sustained matrix-core load the
+MI355X shader clock takes on the order of a second to settle, and a few
+warm-up steps alone time it cold (about a quarter slower).  The phase is
+declared in the output line (``clock_settle``).  Then K steps are timed with
+events on the launch stream (one event between consecutive steps, so the
+mean, median and minimum step times are all reported), bracketed by
+synchronisation.  A shader-clock sample taken on the same stream right
+before and right after the timed steps gives the mean clock over them, and
+the line quotes the percentage of peak both against the published peak
+(2.4 GHz) and against the peak at that measured clock.
 
 Prints one JSON line: the headline metric (forward TFLOP/s, causal FLOPs
 counted as 4*d per visible pair) plus a ``roofline`` object for the kernel and
@@ -31,6 +38,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s at S=8K,d=128 bf16 causal; % of MFMA bf16 peak"
 HEADLINE = "prefill_8k_d128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense: MFMA bf16/f16, fp32 vector
+PEAK_CLOCK_MHZ = 2400.0  # the clock the published peaks assume
 HBM_PEAK_GBS = 8000.0
 # Backward FLOPs: five products of 2*d FLOPs per visible (row, key) pair (S and
 # dP recomputed once, dV, dK, dQ) against the forward's two, the usual
@@ -76,14 +84,133 @@ def measured_traffic(workload: str, sources=FWD_SOURCES):
         return None
 
 
+def host_cpu() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, the CPUs this process
+    may use, and the model name."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"host_cpus": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def blas_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+
+
+class ClockSampler:
+    """Mean shader clock over a stretch of stream work, from the per-die
+    cycle and real-time counters (libfa_clock.so, measurement support)."""
+
+    N_WG = 1024  # work-groups per sample: almost every compute unit gets some
+
+    def __init__(self, device, stream):
+        import ctypes
+
+        import torch
+        path = os.path.join(ROOT, "io_aware_tiled_flash_amd", "libfa_clock.so")
+        self.lib = ctypes.CDLL(path)
+        self.lib.fa_clock_sample.restype = ctypes.c_int
+        self.lib.fa_clock_sample.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        self.lib.fa_clock_realtime_khz.restype = ctypes.c_int
+        self.real_khz = self.lib.fa_clock_realtime_khz()
+        self.bufs = [torch.zeros(3 * self.N_WG, dtype=torch.int64, device=device)
+                     for _ in range(2)]
+        self.stream = stream
+
+    def sample(self, i: int) -> None:
+        st = self.lib.fa_clock_sample(self.bufs[i].data_ptr(), self.N_WG,
+                                      self.stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"clock sample launch failed ({st})")
+
+    def mean_mhz(self):
+        """Mean clock (MHz) between samples 0 and 1: per compute unit seen in
+        both samples (cycle counters of different units are not aligned),
+        then the mean over units, and per die."""
+        if self.real_khz <= 0:
+            return None
+        a, b = (x.cpu().view(-1, 3).tolist() for x in self.bufs)
+        first, last = {}, {}
+        for cu, cyc, real in a:
+            first.setdefault(cu, (cyc, real))
+        for cu, cyc, real in b:
+            last.setdefault(cu, (cyc, real))
+        per_cu = {}
+        for cu in set(first) & set(last):
+            dc = last[cu][0] - first[cu][0]
+            dr = last[cu][1] - first[cu][1]
+            if dr > 0 and dc > 0:
+                per_cu[cu] = dc / (dr / (self.real_khz * 1e3)) / 1e6
+        if not per_cu:
+            return None
+        dies = {}
+        for cu, mhz in per_cu.items():
+            dies.setdefault(cu & 0xF, []).append(mhz)
+        vals = sorted(per_cu.values())
+        return {"mean_MHz": round(sum(vals) / len(vals), 1),
+                "median_MHz": round(vals[len(vals) // 2], 1),
+                "min_MHz": round(vals[0], 1), "max_MHz": round(vals[-1], 1),
+                "compute_units": len(vals),
+                "per_die_MHz": {str(d_): round(sum(v_) / len(v_), 1)
+                                for d_, v_ in sorted(dies.items())},
+                "method": "per compute unit: shader-cycle counter over the real-time counter, "
+                          "sampled on the launch stream right before and after the timed steps"}
+
+
+def time_steps(step, stream, steps: int, warmup: int, settle_s: float, clock=None):
+    """Settle the clock, warm up, then time `steps` calls with one event
+    between consecutive steps.  Returns (step times in ms, settle record)."""
+    import torch
+    settle = {"seconds": 0.0, "steps": 0}
+    if settle_s > 0:
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(10):
+                step()
+            n += 10
+            torch.cuda.synchronize()
+        settle = {"seconds": round(time.perf_counter() - t0, 3), "steps": n}
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    if clock is not None:
+        clock.sample(0)
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    if clock is not None:
+        clock.sample(1)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)], settle
+
+
+def step_stats(ms_list):
+    srt = sorted(ms_list)
+    n = len(srt)
+    med = srt[n // 2] if n % 2 else 0.5 * (srt[n // 2 - 1] + srt[n // 2])
+    return {"mean": round(sum(srt) / n, 4), "median": round(med, 4), "min": round(srt[0], 4),
+            "max": round(srt[-1], 4)}
+
+
 def cpu_baseline(w, q, k, v, target_s: float):
     """Time the fp64 oracle on whole heads of the workload's own (host) inputs
     until ~target_s of wall time has passed."""
-    from threadpoolctl import threadpool_info
-
     from oracle import attention_ref
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    threads = blas_threads()
     per_head_pairs = w.visible_pairs() // (w.B * w.H)
     group = w.H // w.kv_heads
     t0 = time.perf_counter()
@@ -101,16 +228,15 @@ def cpu_baseline(w, q, k, v, target_s: float):
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} heads of {w.name} (all {w.S} query rows each, "
                       f"fp64 numpy, S and P materialised in 2048-row chunks), {el:.1f} s",
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2), "threads": "numpy BLAS threads (the elementwise steps "
+                                                "run on one)", **host_cpu()}
 
 
 def cpu_baseline_bwd(w, q, k, v, do, target_s: float):
     """Time the fp64 oracle's gradients on whole heads until ~target_s."""
-    from threadpoolctl import threadpool_info
-
     from oracle import attention_bwd_rows_ref
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    threads = blas_threads()
     per_head_pairs = w.visible_pairs() // (w.B * w.H)
     group = w.H // w.kv_heads
     t0 = time.perf_counter()
@@ -128,18 +254,17 @@ def cpu_baseline_bwd(w, q, k, v, do, target_s: float):
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"gradients of {heads} of {w.B * w.H} heads of {w.name} (all {w.S} "
                       f"rows, fp64 numpy, P materialised per head), {el:.1f} s",
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2), "threads": "numpy BLAS threads (the elementwise steps "
+                                                "run on one)", **host_cpu()}
 
 
 def cpu_baseline_decode(w, q, kc, vc, table, ctx, target_s: float):
     """Time the fp64 oracle on whole requests until ~target_s; GB/s of the
     same byte accounting as the GPU figure, over the requests it finished."""
-    from threadpoolctl import threadpool_info
-
     from oracle import paged_decode_ref
     from workloads import kv_bytes_per_token
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    threads = blas_threads()
     t0 = time.perf_counter()
     done = []
     while True:
@@ -155,7 +280,8 @@ def cpu_baseline_decode(w, q, kc, vc, table, ctx, target_s: float):
         len(done) * w.H * w.n_q * (2 * w.d * w.esz + 4)
     return {"value": byt / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(done)} of {w.B} requests of {w.name} (every head and row; fp64 "
-                      f"numpy gather + softmax), {el:.1f} s", "seconds": round(el, 2)}
+                      f"numpy gather + softmax), {el:.1f} s", "seconds": round(el, 2),
+            "threads": "numpy BLAS threads (the elementwise steps run on one)", **host_cpu()}
 
 
 def bench_decode(args) -> int:
@@ -187,18 +313,11 @@ def bench_decode(args) -> int:
         if st != fa.FA_OK:
             raise fa.FaError(st, fa.fa_last_error())
 
-    warm = args.warmup if args.warmup_given else 1000
-    for _ in range(warm):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    warm = args.warmup
+    clock = ClockSampler(dev, stream)
+    times, settle = time_steps(step, stream, args.steps, warm, args.settle_s, clock)
+    stats = step_stats(times)
+    ms = stats["mean"]
     c = host[4].numpy()
     byt = w.compulsory_bytes(c)
     gbs = byt / (ms * 1e-3) / 1e9
@@ -229,6 +348,9 @@ def bench_decode(args) -> int:
                      "traffic": measured_traffic(w.name, DECODE_SOURCES),
                      "scope": "whole call (one launch without splits, two with)"},
         "attention_TFLOPs": round(tflops, 2),
+        "step_ms": stats,
+        "clock_settle": settle,
+        "clock": clock.mean_mhz(),
     }
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline_decode(w, *host, args.cpu_seconds)
@@ -260,7 +382,10 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of repeated steps before the warm-up, so that the shader "
+                         "clock reaches its loaded level (declared in the output; 0: none)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "decode"), default="fwd",
                     help="time the forward pass (the headline), the backward pass, or "
@@ -271,7 +396,6 @@ def main() -> int:
                     help="instead of attention, run a plain device-to-device copy of this "
                          "many MiB per step (reference for HBM byte counters)")
     args = ap.parse_args()
-    args.warmup_given = any(a == "--warmup" or a.startswith("--warmup=") for a in sys.argv[1:])
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -323,17 +447,11 @@ def main() -> int:
             if st != fa.FA_OK:
                 raise fa.FaError(st, fa.fa_last_error())
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    clock = ClockSampler(dev, stream)
+    times, settle = time_steps(step, stream, args.steps, args.warmup, args.settle_s, clock)
+    stats = step_stats(times)
+    ms = stats["mean"]
+    clk = clock.mean_mhz()
 
     bwd = args.pass_ == "bwd"
     flops = w.flops() * (BWD_FLOP_RATIO if bwd else 1.0)
@@ -369,10 +487,20 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": traffic},
+        "step_ms": stats,
+        "clock_settle": settle,
+        "clock": clk,
         "hbm": {"compulsory_bytes": w.compulsory_bytes(),
                 "compulsory_GBps": round(w.compulsory_bytes() / (ms * 1e-3) / 1e9, 1),
                 "peak_GBps": HBM_PEAK_GBS},
     }
+    if clk is not None:
+        # the same peak rate per clock (256 CUs x 4096 flop/clk for bf16/fp16
+        # MFMA) at the clock measured over the timed steps
+        peak_at = peak * clk["mean_MHz"] / PEAK_CLOCK_MHZ
+        result["pct_of_peak_at_measured_clock"] = round(100.0 * tflops / peak_at, 2)
+        result["roofline"]["peak_at_measured_clock"] = round(peak_at, 1)
+        result["roofline"]["frac_at_measured_clock"] = round(tflops / peak_at, 4)
     if bwd:
         result["roofline"]["scope"] = "whole pass (three launches)"
     if args.cpu_seconds > 0:

@@ -22,6 +22,10 @@ LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
 SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_f32.hip", "fa_bwd_mfma.hip", "fa_decode.hip"]
+# Measurement support for the benchmark (shader-clock sampler), kept out of
+# the attention library's ABI.
+CLOCK_LIB = os.path.join(PKG, "libfa_clock.so")
+CLOCK_SOURCES = ["fa_clock.hip"]
 
 # Per-source extra flags for the matrix-core kernel:
 #  * it never produces or consumes NaN (masked scores are -inf, which stays
@@ -67,18 +71,35 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def device_asm(src: str, out: str) -> str:
+    """Device assembly of one source, compiled with exactly the library's
+    flags (for checks of the generated code; the library is not touched)."""
+    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stderr}")
+    return out
+
+
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CLOCK_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CLOCK_SOURCES], CLOCK_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CLOCK_LIB}")
     return LIB
 
 
