@@ -239,6 +239,38 @@ fa_status fa_decode_paged(const void *q, const void *k_cache, const void *v_cach
                           float scale, void *stream);
 
 /*
+ * fa_decode_paged_noalloc -- fa_decode_paged for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It takes no workspace argument and allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library call): the split
+ * workspace is a static device array of FA_NOALLOC_SCRATCH_BYTES that the
+ * library owns, one copy per GPU, held until the process ends.  Its device
+ * address is looked up once per device, on the first call made with that
+ * device current.
+ *
+ * Arguments, results, ownership of the caller's buffers and every error of
+ * fa_decode_paged apply (without the workspace rules), and the kernels and
+ * results are the same, bit for bit.  In addition:
+ *   FA_EINVAL  the sizes need a split workspace larger than
+ *              FA_NOALLOC_SCRATCH_BYTES (fa_decode_workspace_size reports
+ *              the need; such sizes must use fa_decode_paged);
+ *   FA_EHIP    the scratch's device address could not be looked up.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's partial results: calls whose executions overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * may return wrong results.  Calls ordered on one stream are safe.  No part
+ * of the scratch needs to start cleared: the kernels write every slot they
+ * read within the same call.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+fa_status fa_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_table, const int32_t *ctx_lens, void *o,
+                                  float *lse, int64_t B, int64_t H, int64_t Hkv, int64_t n_q,
+                                  int64_t d, int64_t num_blocks, int64_t block_size,
+                                  int64_t max_blocks, int64_t max_ctx, int dtype, float scale,
+                                  void *stream);
+
+/*
  * fa_decode_workspace_size -- bytes of workspace fa_decode_paged needs for
  * these sizes (written to *bytes; 0 when none).  Same size checks and error
  * codes as fa_decode_paged; touches no device memory.

@@ -2,7 +2,7 @@
 ``libfa.so``.
 
 The functions ``fa_fwd``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_decode_paged``,
-``fa_decode_workspace_size``, ``fa_query``,
+``fa_decode_paged_noalloc``, ``fa_decode_workspace_size``, ``fa_query``,
 ``fa_status_str``, ``fa_last_error`` and ``fa_abi_version`` mirror the C ABI
 declared in ``include/fa.h`` one to one (argument marshalling only).  ``forward``,
 ``backward`` and ``decode`` are the tensor-level convenience wrappers: they
@@ -18,7 +18,7 @@ import math
 import os
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_decode_paged",
-           "fa_decode_workspace_size",
+           "fa_decode_paged_noalloc", "fa_decode_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "fa_query", "fa_status_str", "fa_last_error", "fa_abi_version", "forward", "backward", "decode", "library_path", "DTYPES", "MASKS",
            "FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
 
@@ -26,6 +26,7 @@ FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 MASKS = {"none": 0, "causal": 1, "window": 2}
 ABI_VERSION = 1
+NOALLOC_SCRATCH_BYTES = 16 << 20  # FA_NOALLOC_SCRATCH_BYTES
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libfa.so"
@@ -65,6 +66,9 @@ def _load():
     lib.fa_decode_paged.restype = c_int
     lib.fa_decode_paged.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_size_t] + [i64] * 9 +
                                     [c_int, ctypes.c_float, ctypes.c_void_p])
+    lib.fa_decode_paged_noalloc.restype = c_int
+    lib.fa_decode_paged_noalloc.argtypes = ([ctypes.c_void_p] * 7 + [i64] * 9 +
+                                            [c_int, ctypes.c_float, ctypes.c_void_p])
     lib.fa_decode_workspace_size.restype = c_int
     lib.fa_decode_workspace_size.argtypes = [i64] * 9 + [c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_query.restype = c_int
@@ -123,6 +127,18 @@ def fa_decode_paged(q: int, k_cache: int, v_cache: int, block_table: int, ctx_le
                                    workspace, workspace_bytes, B, H, Hkv, n_q, d, num_blocks,
                                    block_size, max_blocks, max_ctx, dtype,
                                    ctypes.c_float(scale), stream)
+
+
+def fa_decode_paged_noalloc(q: int, k_cache: int, v_cache: int, block_table: int,
+                            ctx_lens: int, o: int, lse: int, B: int, H: int, Hkv: int, n_q: int,
+                            d: int, num_blocks: int, block_size: int, max_blocks: int,
+                            max_ctx: int, dtype: int, scale: float, stream: int | None) -> int:
+    """Raw paged-cache decode with the library's own split scratch (no
+    workspace argument, nothing allocated); returns the status."""
+    return _load().fa_decode_paged_noalloc(q, k_cache, v_cache, block_table, ctx_lens, o, lse,
+                                           B, H, Hkv, n_q, d, num_blocks, block_size,
+                                           max_blocks, max_ctx, dtype, ctypes.c_float(scale),
+                                           stream)
 
 
 def fa_decode_workspace_size(B: int, H: int, Hkv: int, n_q: int, d: int, num_blocks: int,

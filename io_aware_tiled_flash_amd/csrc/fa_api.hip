@@ -15,6 +15,17 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
+// Split workspace of fa_decode_paged_noalloc: device memory the library owns,
+// so that callers which cannot allocate (code under graph capture, tight
+// serving loops) need not pass any.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code this name is only a
+// stand-in for the symbol: its device address on the current device comes
+// from hipGetSymbolAddress (decode_scratch below), and only that address is
+// ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512];
@@ -285,12 +296,39 @@ fa_status decode_sizes(int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t d
   return FA_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+fa_status decode_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_EUNSUPPORTED, "device %d is beyond the %d devices the scratch table holds",
+                dev, kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return fail(FA_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(g_scratch_err[dev]));
+  *ptr = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+// The decode launch.  With use_scratch the split workspace is the library's
+// own `scratch` (workspace and workspace_bytes are ignored), else the
+// caller's.
 fa_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
                       void *workspace, size_t workspace_bytes, int64_t B, int64_t H,
                       int64_t Hkv, int64_t n_q, int64_t d, int64_t num_blocks,
                       int64_t block_size, int64_t max_blocks, int64_t max_ctx, int dtype,
-                      float scale, void *stream) {
+                      float scale, void *stream, bool use_scratch) {
   g_err[0] = '\0';
   const void *need16[4] = {q, k_cache, v_cache, o};
   for (int i = 0; i < 4; ++i) {
@@ -313,7 +351,14 @@ fa_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
   fa_status st = decode_sizes(B, H, Hkv, n_q, d, num_blocks, block_size, max_blocks, max_ctx,
                               dtype, &sh, &cap, &plan);
   if (st != FA_OK) return st;
-  if (plan.ws_bytes > 0) {
+  if (use_scratch) {
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (plan.ws_bytes > (int64_t)FA_NOALLOC_SCRATCH_BYTES)
+      return fail(FA_EINVAL, "these sizes need %lld bytes of split workspace, more than the "
+                  "%lld-byte scratch of fa_decode_paged_noalloc (use fa_decode_paged with a "
+                  "workspace)", (long long)plan.ws_bytes, (long long)FA_NOALLOC_SCRATCH_BYTES);
+  } else if (plan.ws_bytes > 0) {
     if (!workspace || (uintptr_t)workspace % 16 != 0)
       return fail(FA_EINVAL, "this launch needs a 16-byte-aligned workspace of %lld bytes",
                   (long long)plan.ws_bytes);
@@ -328,7 +373,8 @@ fa_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
   const void *ins[5] = {q, k_cache, v_cache, block_table, ctx_lens};
   const int64_t in_n[5] = {q_bytes, cache_bytes, cache_bytes, table_bytes, ctx_bytes};
   const void *outs[3] = {o, lse, workspace};
-  const int64_t out_n[3] = {q_bytes, lse_bytes, plan.ws_bytes};
+  // (the library's own scratch cannot overlap the caller's buffers)
+  const int64_t out_n[3] = {q_bytes, lse_bytes, use_scratch ? 0 : plan.ws_bytes};
   static const char *out_names[3] = {"o", "lse", "workspace"};
   for (int i = 0; i < 3; ++i) {
     if (out_n[i] == 0) continue;
@@ -338,6 +384,11 @@ fa_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
     for (int j = i + 1; j < 3; ++j)
       if (out_n[j] > 0 && overlaps(outs[i], out_n[i], outs[j], out_n[j]))
         return fail(FA_EINVAL, "%s and %s overlap", out_names[i], out_names[j]);
+  }
+
+  if (use_scratch && plan.ws_bytes > 0) {
+    st = decode_scratch(&workspace);
+    if (st != FA_OK) return st;
   }
 
   fa::DecodeArgs a;
@@ -413,7 +464,18 @@ fa_status fa_decode_paged(const void *q, const void *k_cache, const void *v_cach
                           float scale, void *stream) {
   return decode_impl(q, k_cache, v_cache, block_table, ctx_lens, o, lse, workspace,
                      workspace_bytes, B, H, Hkv, n_q, d, num_blocks, block_size, max_blocks,
-                     max_ctx, dtype, scale, stream);
+                     max_ctx, dtype, scale, stream, false);
+}
+
+fa_status fa_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_table, const int32_t *ctx_lens, void *o,
+                                  float *lse, int64_t B, int64_t H, int64_t Hkv, int64_t n_q,
+                                  int64_t d, int64_t num_blocks, int64_t block_size,
+                                  int64_t max_blocks, int64_t max_ctx, int dtype, float scale,
+                                  void *stream) {
+  return decode_impl(q, k_cache, v_cache, block_table, ctx_lens, o, lse, nullptr, 0, B, H, Hkv,
+                     n_q, d, num_blocks, block_size, max_blocks, max_ctx, dtype, scale, stream,
+                     true);
 }
 
 fa_status fa_decode_workspace_size(int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t d,

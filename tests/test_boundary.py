@@ -29,8 +29,9 @@ def _declared_functions():
 
 def test_library_builds_and_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == ["fa_abi_version", "fa_bwd", "fa_decode_paged", "fa_decode_workspace_size",
-                     "fa_fwd", "fa_fwd_gqa", "fa_last_error", "fa_query", "fa_status_str"]
+    assert names == ["fa_abi_version", "fa_bwd", "fa_decode_paged", "fa_decode_paged_noalloc",
+                     "fa_decode_workspace_size", "fa_fwd", "fa_fwd_gqa", "fa_last_error",
+                     "fa_query", "fa_status_str"]
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -270,6 +271,38 @@ def test_decode_workspace_rules():
     assert st == fa.FA_EUNSUPPORTED  # size checks come first; nothing launched
     st = _call_decode(workspace=A + 16 * MB + 1024, **long)
     assert st == fa.FA_EINVAL and "workspace overlaps" in fa.fa_last_error()
+
+
+NOALLOC_ORDER = [n for n in DEC_ORDER if n not in ("workspace", "workspace_bytes")]
+
+
+def _call_noalloc(**kw):
+    args = dict(DEC)
+    args.update(kw)
+    return fa.fa_decode_paged_noalloc(*[args[n] for n in NOALLOC_ORDER])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(q=0), "null"), (dict(k_cache=A + 16 * MB + 8), "aligned"), (dict(B=0), "sizes"),
+    (dict(Hkv=3), "divide"), (dict(scale=float("nan")), "finite"),
+    (dict(o=A + 16 * MB + 4096), "o overlaps"),
+    (dict(max_blocks=1 << 28, block_size=1024), "index range"),
+])
+def test_noalloc_decode_validates_like_decode(kw, needle):
+    assert _call_noalloc(**kw) == fa.FA_EINVAL
+    assert needle in fa.fa_last_error()
+
+
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch():
+    # 8 requests x 64 query heads x 64 splits of a 256K-token context x 129
+    # floats: 16.9 MB of split workspace, above the 16 MiB scratch; refused
+    # before any HIP call
+    big = dict(B=8, H=64, Hkv=8, max_ctx=262144, max_blocks=16384)
+    need = _ws(**big)
+    assert need > fa.NOALLOC_SCRATCH_BYTES
+    assert _call_noalloc(**big) == fa.FA_EINVAL
+    assert "scratch" in fa.fa_last_error() and str(need) in fa.fa_last_error()
+    assert _call_noalloc(d=96, **big) == fa.FA_EUNSUPPORTED  # size checks come first
 
 
 def test_decode_refuses_host_tensors():
