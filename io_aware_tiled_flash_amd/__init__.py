@@ -40,7 +40,10 @@ class FaError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_PKG, _LIB_NAME)
+    """The in-tree libfa.so, or another build of the same sources named by
+    the environment variable IO_AWARE_FA_LIBRARY (for instance one whose host
+    code is compiled with AddressSanitizer)."""
+    return os.environ.get("IO_AWARE_FA_LIBRARY") or os.path.join(_PKG, _LIB_NAME)
 
 
 def _load():
