@@ -294,6 +294,20 @@ fa_status fa_decode_workspace_size(int64_t B, int64_t H, int64_t Hkv, int64_t n_
 fa_status fa_query(int64_t d, int dtype, int mask, char *kernel_name, size_t len);
 
 /*
+ * fa_query_fwd -- like fa_query, for the sizes of one fa_fwd / fa_fwd_gqa
+ * call: names the kernel instance that call would launch (the instance can
+ * depend on the sizes: grids too small to fill the chip split the keys of
+ * each query tile over several waves) and, when grid is not NULL, stores its
+ * number of work-groups.  Launches nothing and touches no device.  Returns
+ * FA_OK, FA_EINVAL (the size, enum and window checks of fa_fwd) or
+ * FA_EUNSUPPORTED.  Same purpose as fa_query (Dev.to, "Using it in
+ * practice", "Verify the dispatch").
+ */
+fa_status fa_query_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t d, int dtype,
+                       int mask, int64_t window, char *kernel_name, size_t len,
+                       int64_t *grid);
+
+/*
  * fa_status_str -- static English text for a status code (never NULL).
  * fa_last_error -- detail of the last non-OK status returned on the calling
  * thread ("" if none), e.g. which (dtype, head size) has no kernel; the

@@ -3,13 +3,13 @@
 
 The functions ``fa_fwd``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_decode_paged``,
 ``fa_decode_paged_noalloc``, ``fa_decode_workspace_size``, ``fa_query``,
-``fa_status_str``, ``fa_last_error`` and ``fa_abi_version`` mirror the C ABI
-declared in ``include/fa.h`` one to one (argument marshalling only).  ``forward``,
-``backward`` and ``decode`` are the tensor-level convenience wrappers: they
-check the tensors, allocate the outputs with torch and launch on torch's
-current stream.  Every arithmetic step runs in the HIP
-kernels; there is no Python or CPU fallback, and a missing library is an
-error.
+``fa_query_fwd``, ``fa_status_str``, ``fa_last_error`` and ``fa_abi_version``
+mirror the C ABI declared in ``include/fa.h`` one to one (argument
+marshalling only).  ``forward``, ``backward`` and ``decode`` are the
+tensor-level convenience wrappers: they check the tensors, allocate the
+outputs with torch and launch on torch's current stream.  Every arithmetic
+step runs in the HIP kernels; there is no Python or CPU fallback, and a
+missing library is an error.
 """
 from __future__ import annotations
 
@@ -19,8 +19,9 @@ import os
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_decode_paged",
            "fa_decode_paged_noalloc", "fa_decode_workspace_size", "NOALLOC_SCRATCH_BYTES",
-           "fa_query", "fa_status_str", "fa_last_error", "fa_abi_version", "forward", "backward", "decode", "library_path", "DTYPES", "MASKS",
-           "FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
+           "fa_query", "fa_query_fwd", "fa_status_str", "fa_last_error", "fa_abi_version",
+           "forward", "backward", "decode", "library_path", "DTYPES", "MASKS", "FA_OK",
+           "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
 
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
@@ -76,6 +77,9 @@ def _load():
     lib.fa_decode_workspace_size.argtypes = [i64] * 9 + [c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_query.restype = c_int
     lib.fa_query.argtypes = [i64, c_int, c_int, ctypes.c_char_p, ctypes.c_size_t]
+    lib.fa_query_fwd.restype = c_int
+    lib.fa_query_fwd.argtypes = [i64] * 5 + [c_int, c_int, i64, ctypes.c_char_p,
+                                             ctypes.c_size_t, ctypes.POINTER(i64)]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [c_int]
     lib.fa_last_error.restype = ctypes.c_char_p
@@ -162,6 +166,19 @@ def fa_query(d: int, dtype: int, mask: int) -> str:
     if st != FA_OK:
         raise FaError(st, fa_last_error())
     return buf.value.decode()
+
+
+def fa_query_fwd(B: int, H: int, Hkv: int, S: int, d: int, dtype: int, mask: int,
+                 window: int = 0) -> tuple[str, int]:
+    """(kernel instance, work-groups) that fa_fwd / fa_fwd_gqa would launch
+    for these sizes; raises on error."""
+    buf = ctypes.create_string_buffer(160)
+    grid = ctypes.c_int64(0)
+    st = _load().fa_query_fwd(B, H, Hkv, S, d, dtype, mask, window, buf, len(buf),
+                              ctypes.byref(grid))
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return buf.value.decode(), grid.value
 
 
 def fa_status_str(status: int) -> str:

@@ -513,6 +513,43 @@ fa_status fa_query(int64_t d, int dtype, int mask, char *kernel_name, size_t len
   return FA_OK;
 }
 
+fa_status fa_query_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t d, int dtype,
+                       int mask, int64_t window, char *kernel_name, size_t len,
+                       int64_t *grid) {
+  g_err[0] = '\0';
+  if (B < 1 || H < 1 || Hkv < 1 || S < 1 || d < 1)
+    return fail(FA_EINVAL, "sizes must be >= 1");
+  if (H % Hkv != 0) return fail(FA_EINVAL, "key/value heads must divide query heads");
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_EINVAL, "unknown dtype %d", dtype);
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_WINDOW)
+    return fail(FA_EINVAL, "unknown mask %d", mask);
+  if (mask == FA_MASK_WINDOW && window < 1) return fail(FA_EINVAL, "window must be >= 1");
+  if (len > 0 && !kernel_name) return fail(FA_EINVAL, "null name buffer");
+  int64_t bh;
+  if (!mul_ok(B, H, &bh) || bh > (int64_t)INT32_MAX || S > (int64_t)INT32_MAX ||
+      d > (int64_t)INT32_MAX)
+    return fail(FA_EINVAL, "sizes too large");
+  const int eff_mask = (mask == FA_MASK_WINDOW && window >= S) ? FA_MASK_CAUSAL : mask;
+  fa::FwdArgs a = {};
+  a.B = (int)B;
+  a.H = (int)H;
+  a.Hkv = (int)Hkv;
+  a.S = (int)S;
+  a.window = eff_mask == FA_MASK_WINDOW ? (int)window : 0;
+  fa::LaunchInfo info = {nullptr, 0, 0};
+  hipError_t err = hipSuccess;
+  if (!dispatch(dtype, (int)d, eff_mask, &a, nullptr, false, &info, &err))
+    return fail(FA_EUNSUPPORTED, "no kernel for dtype=%s d=%lld", dtype_name(dtype),
+                (long long)d);
+  if (len > 0) {
+    strncpy(kernel_name, info.name, len - 1);
+    kernel_name[len - 1] = '\0';
+  }
+  if (grid) *grid = (S + info.block_rows - 1) / info.block_rows * bh;
+  return FA_OK;
+}
+
 const char *fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

@@ -59,13 +59,30 @@
 //     result is unchanged up to rounding (the deferred-rescaling idea of the
 //     "What FlashAttention-2 changed" section, taken one step further: the
 //     common path computes no row maximum at all);
-//   * l accumulates the fp32 weights (before they are rounded to the input
-//     dtype for the PV product), so the logsumexp is not limited by bf16
-//     precision;
+//   * l sums the fp32 weights (before they are rounded to the input dtype
+//     for the PV product), so the logsumexp is not limited by bf16
+//     precision.  The key-split instances (small grids) also keep lt, the
+//     sum of the rounded weights the PV product actually used, and
+//     normalise O by it: O is then an exact convex combination of V rows
+//     with weights p~/sum p~, and a row dominated by one key returns that
+//     key's V row exactly, where dividing by the fp32 sum carries the
+//     dominant weight's rounding (up to 2^-8 of |V| in bf16, when the lazy
+//     offset left that weight inexact) into O.  The other instances divide
+//     by l: the second sum costs about 7% of their throughput;
 //   * heavy query tiles (the last ones, under a causal or window mask) are
 //     dispatched first; consecutive work-groups take different heads, so with
 //     the round-robin placement over the 8 XCDs all query tiles of one head
-//     land on the same XCD and share its L2.
+//     land on the same XCD and share its L2;
+//   * grids too small to fill the chip split the keys as well: the waves of
+//     a work-group form NR row groups times NK key groups, key group g takes
+//     every NK-th key tile of the work-group's band (each group with LDS
+//     stages of its own, all groups in step), and at the end the NK partial
+//     results of each row are merged through LDS with the same rescaling
+//     algebra (m = max m_g, l = sum l_g 2^(m_g - m), O = sum O_g 2^(m_g - m)
+//     / l).  This is the extra parallelism over the sequence of the chapter's
+//     "What FlashAttention-2 changed" section, taken along the keys, so that
+//     a short sequence's last query tile no longer runs all of its key tiles
+//     one after another on one wave.
 #include "fa_gfx950.h"
 
 #include <math.h>
@@ -98,24 +115,23 @@ template <class Ty> struct WeightCap;
 template <> struct WeightCap<TBF16> { static constexpr float value = 4294967296.0f; };
 template <> struct WeightCap<TF16> { static constexpr float value = 256.0f; };
 
-#ifndef FA_RPD
-#define FA_RPD 2
-#endif
-
-template <class Ty, int D, int MASK, int NW, int BC, int NH, int PF>
+template <class Ty, int D, int MASK, int NW, int NK, int BC, int NH, int PF>
 __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
+  constexpr int NR = NW / NK;          // row groups (one wave each per key group)
   constexpr int QW = 32 * NH;          // query rows per wave
-  constexpr int BR = QW * NW;          // query rows per work-group
+  constexpr int BR = QW * NR;          // query rows per work-group
   constexpr int NKB = BC / 32;         // 32-key blocks per key tile
   constexpr int NKS = D / 16;          // contraction steps of S^T = K Q^T
   constexpr int NDB = D / 32;          // 32-wide d blocks of O^T
   constexpr int NPS = BC / 16;         // contraction steps of O^T = V^T P^T
   constexpr int KCH = D / 8;           // 16-byte chunks per K/V row
   constexpr int TILE_CHUNKS = BC * KCH;  // 16-byte chunks per K or V tile
-  constexpr int LOADS_PER_WAVE = TILE_CHUNKS / 64 / NW;  // direct loads per tensor
+  // The NR waves of a key group load its tiles together.
+  constexpr int LOADS_PER_WAVE = TILE_CHUNKS / 64 / NR;  // direct loads per tensor
+  static_assert(NW % NK == 0, "key groups must split the waves evenly");
   static_assert(D % 32 == 0 && BC % 32 == 0 && BC % 16 == 0, "tile shape");
   static_assert(KCH >= 8, "swizzle needs >= 8 chunks per LDS row");
-  static_assert(TILE_CHUNKS % (64 * NW) == 0, "tile must split evenly over the waves");
+  static_assert(TILE_CHUNKS % (64 * NR) == 0, "tile must split evenly over a group's waves");
 
   // Tiles are loaded PF tiles ahead of the one being computed.  K needs PF+1
   // stages; V needs PF+2 because the PV products of tile t are issued during
@@ -125,16 +141,20 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // LDS instructions.
   constexpr int NST = PF + 2;
   static_assert(NST == 4, "the tile loop below is unrolled four times");
-  constexpr int NKST = NST, NVST = NST;
+  constexpr int NVST = NST;
   constexpr int LOADS_PER_TILE = 2 * LOADS_PER_WAVE;  // per wave, K and V
   static_assert(LOADS_PER_TILE * (PF - 1) < 64, "vmcnt range");
-  __shared__ u32x4 k_lds[NKST][TILE_CHUNKS];
-  __shared__ u32x4 v_lds[NVST][TILE_CHUNKS];
+  // K and V stages per key group (separate arrays: each operand read's LDS
+  // offset then stays within the 16-bit immediate of the instruction).
+  __shared__ u32x4 k_lds[NK][NST][TILE_CHUNKS];
+  __shared__ u32x4 v_lds[NK][NST][TILE_CHUNKS];
 
   const int tid = threadIdx.x;
   // readfirstlane makes the wave index (and everything derived from it) a
   // scalar, so per-wave tile decisions become scalar branches.
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // row group and key group (compile-time 0 without a key split)
+  const int rg = NK == 1 ? wave : wave % NR, kg = NK == 1 ? 0 : wave / NR;
   const int lq = lane & 31, lg = lane >> 5;
   const int S = a.S;
   const int BH = a.B * a.H;
@@ -162,7 +182,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q^T as the B operand: lane holds Q[row][16*ks + 8*lg .. +7] for every ks.
-  const int wr0 = q0 + wave * QW;  // first query row of this wave
+  const int wr0 = q0 + rg * QW;    // first query row of this wave
   const int wr1 = wr0 + QW - 1;    // last query row of this wave
   u32x4 qreg[NH][NKS];
 #pragma unroll
@@ -189,19 +209,20 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // Direct loads of tile kt into K stage kst and V stage vst.  Chunk position
   // p of a stage holds row p / KCH, logical chunk c with swz(row, c) == p % KCH
   // (swz is an involution in c).
-  // LDS byte address of this wave's first 64-chunk block in stage 0 of K and
-  // of V: wave-uniform, so every direct load's LDS address is a scalar plus
-  // a compile-time offset.
+  // LDS byte address of this wave's first 64-chunk block in stage 0 of its
+  // key group's K and V: wave-uniform, so every direct load's LDS address is
+  // a scalar plus a compile-time offset.
   const uint32_t k_lds0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)&k_lds[0][64 * wave * LOADS_PER_WAVE]);
+      (uint32_t)(uintptr_t)&k_lds[kg][0][64 * rg * LOADS_PER_WAVE]);
   const uint32_t v_lds0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)&v_lds[0][64 * wave * LOADS_PER_WAVE]);
+      (uint32_t)(uintptr_t)&v_lds[kg][0][64 * rg * LOADS_PER_WAVE]);
   constexpr uint32_t STAGE_BYTES = TILE_CHUNKS * 16;
+  constexpr uint32_t GROUP_BYTES = NST * STAGE_BYTES;  // one key group's stages
   auto load_tile = [&](int kt, int kst, int vst) __attribute__((always_inline)) {
     const int k0 = kt * BC;
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      const int blk = wave * LOADS_PER_WAVE + i;  // 64-chunk block of the tile
+      const int blk = rg * LOADS_PER_WAVE + i;  // 64-chunk block of the tile
       const int pos = 64 * blk + lane;
       const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
       const uint32_t off = (uint32_t)((k0 + r) * D + 8 * cc) * 2u;
@@ -213,8 +234,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   f32x16 oacc[NH][NDB];
   f32x16 sacc[NH][NKB];
   u32x4 pk[NH][NPS];  // packed weights of the previous tile, awaiting their PV product
-  float m[NH], l[NH];
-  float m_use[NH], lpart[NH];  // offset the exponent arguments use; a tile's weight sum
+  float m[NH], l[NH], lt[NH];
+  float m_use[NH], lpart[NH], ltpart[NH];  // offset the exponents use; a tile's weight sums
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
 #pragma unroll
@@ -222,9 +243,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NPS; ++i) pk[h][i] = u32x4{};
     m[h] = -INFINITY;  // running offset, base 2 (equal in lanes q and q^32)
-    l[h] = 0.f;        // this lane's share of the running denominator
+    l[h] = 0.f;        // this lane's share of the running denominator (fp32 weights)
+    lt[h] = 0.f;       // the same over the rounded weights
     m_use[h] = 0.f;
     lpart[h] = -0.f;
+    ltpart[h] = -0.f;
   }
   // O accumulators and scores stay in VGPRs (the file is built with the
   // VGPR-destination MFMA form): the softmax and the rare rescale then read
@@ -235,12 +258,16 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 
   // Per-lane LDS byte offsets.  The swizzle XOR is split into a per-lane base
   // and a compile-time part so every operand read is "lane pointer +
-  // immediate".  K operand of step ks, key block kb: row 32*kb + lq, logical
-  // chunk 2*ks + lg; one base per ks % KSW.
+  // immediate"; the bases include the offset of the wave's key group, so
+  // operand reads address the stages as those of key group 0.  K operand of
+  // step ks, key block kb: row 32*kb + lq, logical chunk 2*ks + lg; one base
+  // per ks % KSW.
   constexpr int KSW = D >= 128 ? 8 : 4;
+  const int group_off = kg * (int)GROUP_BYTES;
   int k_base[KSW];
 #pragma unroll
-  for (int j = 0; j < KSW; ++j) k_base[j] = lq * (D * 2) + 16 * swz<D>(lq, 2 * j + lg);
+  for (int j = 0; j < KSW; ++j)
+    k_base[j] = group_off + lq * (D * 2) + 16 * swz<D>(lq, 2 * j + lg);
 
   // V^T operand of step kk, d block db, part i2: lane (group G = lane/16,
   // n = lane%16) names row key = 16*kk + 8*i2 + tr_key (tr_key = 4*lg + n/4)
@@ -257,7 +284,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NVB; ++j) {
       const int key = 8 * (j & 1) + tr_key;
-      v_base[j] = key * (D * 2) + 16 * swz<D>(key, 4 * (j >> 1) + tr_c) + 8 * (lane & 1);
+      v_base[j] = group_off + key * (D * 2) + 16 * swz<D>(key, 4 * (j >> 1) + tr_c) +
+                  8 * (lane & 1);
     }
   }
   auto v_off = [](int kk, int db) constexpr { return 16 * kk * (D * 2) + 64 * (db & ~3); };
@@ -282,7 +310,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   };
   // O_h^T += V^T P_h^T for every half, without interleaved work (last tile).
   auto o_phase = [&](int vst) __attribute__((always_inline)) {
-    const char *vl = (const char *)&v_lds[vst][0];
+    const char *vl = (const char *)&v_lds[0][vst][0];
 #pragma unroll
     for (int st = 0; st < NPS * NDB; ++st) {
       const u32x4 op = read_v(vl, st);
@@ -376,24 +404,26 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   constexpr int UAB = 8 < UAB_ALL ? 8 : UAB_ALL;  // weight units phase B makes
   constexpr int UA = NH * NPS * 4 - UAB;       // weight units left to phase A
   constexpr float CAP = WeightCap<Ty>::value;
-  float s4a[NH][4];
+  float s4a[NH][4], s4t[NH][4];  // a tile's partial sums, fp32 and rounded weights
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s4a[h][j] = -0.f;
+    for (int j = 0; j < 4; ++j) s4a[h][j] = s4t[h][j] = -0.f;
   auto sums_start = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s4a[h][j] = -0.f;  // -0 + x == x folds away
+      for (int j = 0; j < 4; ++j) s4a[h][j] = s4t[h][j] = -0.f;  // -0 + x == x folds away
   };
   auto weight_unit = [&](int h, int kk, int j) __attribute__((always_inline)) {
     const float p0 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j]);
     const float p1 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j + 1]);
     pk[h][kk][j] = Ty::pack2(p0, p1);
     s4a[h][j] += p0 + p1;
+    if constexpr (NK > 1) s4t[h][j] = Ty::add2(pk[h][kk][j], s4t[h][j]);
     pin(pk[h][kk][j]);
     pin(s4a[h][j]);
+    if constexpr (NK > 1) pin(s4t[h][j]);
   };
   // Weight units in step-major order: r -> (half (r/4) % NH, step r/(4 NH),
   // pair r % 4); phase B makes r < UAB, phase A the rest.
@@ -429,7 +459,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       const float alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(-shift);
       if (!(fresh && t == -INFINITY)) m[h] = m_use[h] + shift;
       m_use[h] = m[h] == -INFINITY ? 0.f : m[h];
-      float sum = 0.f;
+      float sum = 0.f, sumt = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NPS; ++kk)
 #pragma unroll
@@ -438,9 +468,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
           const float p1 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j + 1] - shift);
           pk[h][kk][j] = Ty::pack2(p0, p1);
           sum += p0 + p1;
+          if constexpr (NK > 1) sumt = Ty::add2(pk[h][kk][j], sumt);
         }
       lpart[h] = sum;
+      ltpart[h] = sumt;
       l[h] *= alpha;
+      if constexpr (NK > 1) lt[h] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[h][db] *= alpha;
     }
@@ -450,6 +483,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       lpart[h] = (s4a[h][0] + s4a[h][1]) + (s4a[h][2] + s4a[h][3]);
+      if constexpr (NK > 1) ltpart[h] = (s4t[h][0] + s4t[h][1]) + (s4t[h][2] + s4t[h][3]);
       trig = trig || lpart[h] > CAP || m[h] == -INFINITY;
     }
     if (__any(trig)) settle();
@@ -457,6 +491,10 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     for (int h = 0; h < NH; ++h) {
       l[h] += lpart[h];
       pin(l[h]);
+      if constexpr (NK > 1) {
+        lt[h] += ltpart[h];
+        pin(lt[h]);
+      }
     }
   };
 
@@ -490,22 +528,22 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   constexpr int NSA = NKS * NKB, MA = NSA * NH;  // score steps, MFMAs
   constexpr int NSB = NPS * NDB, MB = NSB * NH;  // product steps, MFMAs
   constexpr int NDMA = 2 * LOADS_PER_WAVE;       // direct loads per tile
-  constexpr int RPD = FA_RPD;                    // operand reads run RPD steps ahead
+  constexpr int RPD = 2;                         // operand reads run RPD steps ahead
   constexpr int UA_PRE = 1 < UA ? 1 : UA;        // units before the first MFMA
   // Tile with stage phase P = it % NST: K in stage P, the previous tile's V
   // in stage P-1, loads of tile it+PF into stage P+PF.
   auto tile = [&](bool masked, auto phase_c, int k0, int lkt) __attribute__((always_inline)) {
     constexpr int P = decltype(phase_c)::value;
     constexpr int kst = P, vprev = (P + NST - 1) % NST, lks = (P + PF) % NST, lvs = lks;
-    const char *kl = (const char *)&k_lds[kst][0];
-    const char *vl = (const char *)&v_lds[vprev][0];
+    const char *kl = (const char *)&k_lds[0][kst][0];
+    const char *vl = (const char *)&v_lds[0][vprev][0];
     const int lk0 = lkt * BC;
     // Direct load d of tile t+PF (K and V alternate), issued after MFMA 2d+1
     // of phase A (placements over both phases, or all at once, measured no
     // better).
     auto dma = [&](int d) __attribute__((always_inline)) {
       const int i = d >> 1;
-      const int blk = wave * LOADS_PER_WAVE + i;
+      const int blk = rg * LOADS_PER_WAVE + i;
       const int pos = 64 * blk + lane;
       const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
       const uint32_t off = (uint32_t)((lk0 + r) * D + 8 * cc) * 2u;
@@ -514,8 +552,10 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       else
         load16_to_lds_s(rk, off, k_lds0 + lks * STAGE_BYTES + 1024u * i);
     };
-    auto dma_slot = [](int d) constexpr { return 2 * d + 1; };
-    static_assert(2 * NDMA <= MA, "direct loads must fit between the score MFMAs");
+    // (one per MFMA, from the first, when there are more loads than half the
+    // score MFMAs)
+    auto dma_slot = [](int d) constexpr { return 2 * NDMA <= MA ? 2 * d + 1 : d; };
+    static_assert(NDMA <= MA, "direct loads must fit between the score MFMAs");
     // ---- phase A ----
     u32x4 kop[RPD + 1];
 #pragma unroll
@@ -574,15 +614,18 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 
   // Zero the V stage that the first tile's (empty) pending product reads, so
   // that its zero weights never meet uninitialised LDS.
-  for (int i = tid; i < TILE_CHUNKS; i += NW * 64) v_lds[NVST - 1][i] = u32x4{};
+  for (int i = tid; i < NK * TILE_CHUNKS; i += NW * 64)
+    v_lds[i / TILE_CHUNKS][NVST - 1][i % TILE_CHUNKS] = u32x4{};
   // Prefetches past the last tile read an index beyond the sequence: the
   // buffer range check turns them into zero fills of a free stage, so every
   // tile issues the same number of loads and the waits below are constants
-  // (no branch splits the loop body).
-  const int kt_none = ntk + PF;
+  // (no branch splits the loop body).  Key group g's step `it` is tile
+  // kt_begin + g + NK * it.
+  const int kt_none = ntk + PF * NK;
+  auto tile_of = [&](int it) { return kt_begin + kg + NK * it; };
   auto tile_or_none = [&](int kt) { return kt < kt_end ? kt : kt_none; };
 #pragma unroll
-  for (int i = 0; i < PF; ++i) load_tile(tile_or_none(kt_begin + i), i, i);
+  for (int i = 0; i < PF; ++i) load_tile(tile_or_none(tile_of(i)), i, i);
   // Wait for the first tile only (and the zero fill); the later prefetches
   // stay in flight.
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
@@ -596,19 +639,21 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // reads that run ahead of the MFMAs.
   asm volatile("" ::"s"(rk), "s"(rv), "s"(a.o), "s"(a.lse));
 
-  // The work-group's tiles run in groups of NST, each copy of the tile with
-  // its own compile-time stage phase.  The range is padded to a multiple of
-  // NST with tiles past the last visible one: their loads read the
-  // out-of-range index (zero fill) and all their scores are masked, so they
-  // contribute weight 0 and factor 1 (at most NST-1 such tiles per
-  // work-group; none when the visible range is a multiple of 4 tiles, as
-  // for the 256-row work-groups of a causal sequence).
+  // The work-group's steps run in groups of NST, each copy of the tile with
+  // its own compile-time stage phase.  Every key group takes the same number
+  // of steps (the largest group's share, padded to a multiple of NST) with
+  // tiles past the last visible one: their loads read the out-of-range index
+  // (zero fill) and all their scores are masked, so they contribute weight 0
+  // and factor 1 (none for the 256-row work-groups of a causal sequence,
+  // whose visible range is a multiple of 4 tiles).
   //
-  // Every wave runs every tile of the range (the loads and barriers are
-  // shared).  A wave masks a tile elementwise when the tile straddles an edge
-  // of its rows' band or lies outside it; a tile outside the band is simply
-  // fully masked (weights 0, factor 1).
-  const int n_pad = (kt_end - kt_begin + NST - 1) / NST * NST;
+  // Every wave of a key group runs every tile of that group (the loads are
+  // shared within the group, the barriers by all).  A wave masks a tile
+  // elementwise when the tile straddles an edge of its rows' band or lies
+  // outside it; a tile outside the band is simply fully masked (weights 0,
+  // factor 1).
+  const int n_steps = (kt_end - kt_begin + NK - 1) / NK;
+  const int n_pad = (n_steps + NST - 1) / NST * NST;
   auto need_mask = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BC;
     if (kt >= kt_end) return true;
@@ -621,16 +666,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // barrier extends that to the whole work-group.  Every LDS read of this
   // tile was consumed by an MFMA above, so after the barrier the stages read
   // here may be overwritten.
-  auto step = [&](auto phase_c, int kt) __attribute__((always_inline)) {
-    tile(need_mask(kt), phase_c, kt * BC, tile_or_none(kt + PF));
+  auto step = [&](auto phase_c, int it) __attribute__((always_inline)) {
+    const int kt = tile_of(it);
+    tile(need_mask(kt), phase_c, kt * BC, tile_or_none(tile_of(it + PF)));
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
     __builtin_amdgcn_s_barrier();
   };
-  for (int kt = kt_begin; kt < kt_begin + n_pad; kt += NST) {
-    step(std::integral_constant<int, 0>{}, kt);
-    step(std::integral_constant<int, 1>{}, kt + 1);
-    step(std::integral_constant<int, 2>{}, kt + 2);
-    step(std::integral_constant<int, 3>{}, kt + 3);
+  for (int it = 0; it < n_pad; it += NST) {
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
+    step(std::integral_constant<int, 2>{}, it + 2);
+    step(std::integral_constant<int, 3>{}, it + 3);
   }
   // The last tile: its remaining weights, then its PV products.
 #pragma unroll
@@ -638,13 +684,102 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   a_finish();
   if (n_pad > 0) o_phase(NST - 1);
 
+  // Row statistics of the rows this wave holds: offset m (base 2) and the
+  // full denominators (both lanes of a row).
+  float l_tot[NH], lt_tot[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    l_tot[h] = l[h] + wave_partner(l[h]);
+    lt_tot[h] = NK > 1 ? lt[h] + wave_partner(lt[h]) : l_tot[h];
+  }
+
+  if constexpr (NK > 1) {
+    // Merge of the key groups' partial results, row group by row group, in
+    // key group 0's waves: m = max m_g, l = sum l_g 2^(m_g - m),
+    // O = sum O_g 2^(m_g - m) (a group that saw no visible key of a row has
+    // m_g = -inf and factor 0).  The stages are reused for the partials
+    // (accumulators in the K stages, row statistics in the V stages) once
+    // every wave is done with them and the zero-fill loads still in flight
+    // (past the last tile) have landed.  The partials are stored in the
+    // register layout (16 bytes per lane, consecutive lanes), so the stores
+    // and reads are conflict-free.
+    constexpr int NBLK = NH * NDB;                       // accumulator blocks per wave
+    constexpr int O_BYTES = (NK - 1) * NR * NBLK * 4096;  // 16 floats x 64 lanes each
+    static_assert(O_BYTES <= (int)sizeof(k_lds), "merge space (accumulators)");
+    static_assert((NK - 1) * NR * NH * 1024 <= (int)sizeof(v_lds), "merge space (statistics)");
+    char *mbuf = (char *)&k_lds[0][0][0];
+    char *sbuf = (char *)&v_lds[0][0][0];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (kg > 0) {
+      const int p0 = (kg - 1) * NR + rg;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x16 &o = oacc[h][db];
+            *(f32x4 *)(mbuf + (p0 * NBLK + h * NDB + db) * 4096 + (j * 64 + lane) * 16) =
+                f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
+          }
+        *(f32x4 *)(sbuf + ((p0 * NH + h) * 64 + lane) * 16) =
+            f32x4{m[h], l_tot[h], lt_tot[h], 0.f};
+      }
+    }
+    __builtin_amdgcn_s_barrier();
+    if (kg > 0) return;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      float mg[NK], lgs[NK], ltg[NK];
+      mg[0] = m[h];
+      lgs[0] = l_tot[h];
+      ltg[0] = lt_tot[h];
+      float mm = m[h];
+#pragma unroll
+      for (int g = 1; g < NK; ++g) {
+        const f32x4 ml =
+            *(const f32x4 *)(sbuf + ((((g - 1) * NR + rg) * NH + h) * 64 + lane) * 16);
+        mg[g] = ml[0];
+        lgs[g] = ml[1];
+        ltg[g] = ml[2];
+        mm = fmaxf(mm, mg[g]);
+      }
+      float f[NK], lsum = 0.f, ltsum = 0.f;
+#pragma unroll
+      for (int g = 0; g < NK; ++g) {
+        f[g] = mg[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg[g] - mm);
+        lsum = fmaf(f[g], lgs[g], lsum);
+        ltsum = fmaf(f[g], ltg[g], ltsum);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        f32x16 acc = oacc[h][db] * f[0];
+#pragma unroll
+        for (int g = 1; g < NK; ++g) {
+          const int p = (g - 1) * NR + rg;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 o =
+                *(const f32x4 *)(mbuf + (p * NBLK + h * NDB + db) * 4096 + (j * 64 + lane) * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * j + e] = fmaf(f[g], o[e], acc[4 * j + e]);
+          }
+        }
+        oacc[h][db] = acc;
+      }
+      m[h] = mm;
+      l_tot[h] = lsum;
+      lt_tot[h] = ltsum;
+    }
+  }
+
   // Epilogue: one division per row, RNE to the element type, natural-log LSE.
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int row = wr0 + 32 * h + lq;
-    const float l_tot = l[h] + wave_partner(l[h]);
     if (row < S) {
-      const float inv = 1.f / l_tot;
+      const float inv = 1.f / lt_tot[h];
       uint16_t *orow = (uint16_t *)a.o + head_off + (size_t)row * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -658,36 +793,32 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       }
       if (lg == 0)
         a.lse[(size_t)bh * S + row] =
-            (m[h] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+            (m[h] + __builtin_amdgcn_logf(l_tot[h])) * 0.69314718055994531f;
     }
   }
 }
 
-#ifndef FA_BC64
-#define FA_BC64 64
-#endif
-#ifndef FA_BC128
-#define FA_BC128 32
-#endif
-#ifndef FA_BC256
-#define FA_BC256 32
-#endif
-#ifndef FA_PF
-#define FA_PF 2
-#endif
-template <class Ty, int D, int MASK>
+// One kernel instance: NW waves per work-group as NK key groups of NR = NW/NK
+// row groups.  NK = 1 is the plain decomposition (one work-group per 256
+// query rows at d <= 128); NK > 1 splits each work-group's key tiles over
+// the key groups, for grids too small to fill the chip.
+template <class Ty, int D, int MASK, int NK>
 struct Instance {
   static constexpr int NW = 4;
-  static constexpr int BC = D == 64 ? FA_BC64 : D == 128 ? FA_BC128 : FA_BC256;
+  static constexpr int BC = NK > 1 ? 32 : D == 64 ? 64 : 32;  // keys per tile
   static constexpr int NH = D <= 128 ? 2 : 1;
-  static constexpr int PF = D == 256 && FA_PF > 3 ? 3 : FA_PF;  // LDS budget
-  static constexpr int BR = 32 * NH * NW;
+  static constexpr int PF = 2;
+  static constexpr int BR = 32 * NH * (NW / NK);
   static bool run(const FwdArgs *a, hipStream_t stream, bool launch, LaunchInfo *info,
                   hipError_t *err) {
     static char name[96];
     static const char *mk[3] = {"none", "causal", "window"};
-    snprintf(name, sizeof(name), "fa_fwd_mfma<%s,d%d,%s,br%d,bc%d,pf%d>", Ty::kName, D,
-             mk[MASK], BR, BC, PF);
+    if (NK > 1)
+      snprintf(name, sizeof(name), "fa_fwd_mfma<%s,d%d,%s,br%d,bc%d,pf%d,keysplit%d>",
+               Ty::kName, D, mk[MASK], BR, BC, PF, NK);
+    else
+      snprintf(name, sizeof(name), "fa_fwd_mfma<%s,d%d,%s,br%d,bc%d,pf%d>", Ty::kName, D,
+               mk[MASK], BR, BC, PF);
     info->name = name;
     info->block_rows = BR;
     info->threads = NW * 64;
@@ -697,19 +828,41 @@ struct Instance {
     const dim3 block(NW * 64);
     FwdArgs args = *a;
     void *kargs[] = {&args};
-    *err = hipLaunchKernel((const void *)&fa_fwd_mfma_kernel<Ty, D, MASK, NW, BC, NH, PF>, grid,
-                           block, kargs, 0, stream);
+    *err = hipLaunchKernel((const void *)&fa_fwd_mfma_kernel<Ty, D, MASK, NW, NK, BC, NH, PF>,
+                           grid, block, kargs, 0, stream);
     return true;
   }
 };
+
+// Key groups for a launch of these sizes: 1 unless the plain grid has fewer
+// work-groups than the chip has compute units (256), in which case the keys
+// are split 4 ways at d = 64 (64-row work-groups) and 2 ways at d = 128
+// (128-row work-groups), within the 128 KB of LDS the split stages need.
+constexpr int kComputeUnits = 256;
+template <int D>
+int key_groups(const FwdArgs *a) {
+  if (!a || D > 128) return 1;
+  const int64_t plain = (int64_t)((a->S + 255) / 256) * a->B * a->H;
+  if (plain >= kComputeUnits) return 1;
+  return D == 64 ? 4 : 2;
+}
+
+template <class Ty, int D, int MASK>
+bool by_split(const FwdArgs *a, hipStream_t s, bool launch, LaunchInfo *info, hipError_t *err) {
+  if constexpr (D <= 128) {
+    if (key_groups<D>(a) > 1)
+      return Instance<Ty, D, MASK, D == 64 ? 4 : 2>::run(a, s, launch, info, err);
+  }
+  return Instance<Ty, D, MASK, 1>::run(a, s, launch, info, err);
+}
 
 template <class Ty, int D>
 bool by_mask(int mask, const FwdArgs *a, hipStream_t s, bool launch, LaunchInfo *info,
              hipError_t *err) {
   switch (mask) {
-    case kMaskNone: return Instance<Ty, D, kMaskNone>::run(a, s, launch, info, err);
-    case kMaskCausal: return Instance<Ty, D, kMaskCausal>::run(a, s, launch, info, err);
-    case kMaskWindow: return Instance<Ty, D, kMaskWindow>::run(a, s, launch, info, err);
+    case kMaskNone: return by_split<Ty, D, kMaskNone>(a, s, launch, info, err);
+    case kMaskCausal: return by_split<Ty, D, kMaskCausal>(a, s, launch, info, err);
+    case kMaskWindow: return by_split<Ty, D, kMaskWindow>(a, s, launch, info, err);
   }
   return false;
 }

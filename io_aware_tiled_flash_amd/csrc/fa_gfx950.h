@@ -15,6 +15,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -34,6 +35,12 @@ struct TBF16 {
   __device__ static inline f32x2 unpack2(uint32_t w) {
     return f32x2{__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
   }
+  // acc + both packed values (v_dot2_f32_bf16 against (1, 1): the products
+  // are exact, the sum is an fp32 addition)
+  __device__ static inline float add2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+  }
 };
 
 struct TF16 {
@@ -50,6 +57,11 @@ struct TF16 {
   // the two packed values, exactly, as floats (low half first)
   __device__ static inline f32x2 unpack2(uint32_t w) {
     return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+  }
+  // acc + both packed values (v_dot2_f32_f16 against (1, 1))
+  __device__ static inline float add2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                  __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
   }
 };
 

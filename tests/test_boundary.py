@@ -31,7 +31,7 @@ def test_library_builds_and_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == ["fa_abi_version", "fa_bwd", "fa_decode_paged", "fa_decode_paged_noalloc",
                      "fa_decode_workspace_size", "fa_fwd", "fa_fwd_gqa", "fa_last_error",
-                     "fa_query", "fa_status_str"]
+                     "fa_query", "fa_query_fwd", "fa_status_str"]
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -66,6 +66,27 @@ def test_query_f32(d):
 def test_query_unsupported(d, dtype):
     with pytest.raises(fa.FaError) as e:
         fa.fa_query(d, fa.DTYPES[dtype], 0)
+    assert e.value.status == fa.FA_EUNSUPPORTED
+
+
+def test_query_fwd_names_the_instance_for_the_sizes():
+    # large grids: the plain instance, one work-group per 256 query rows
+    name, grid = fa.fa_query_fwd(1, 32, 32, 8192, 128, fa.DTYPES["bf16"], fa.MASKS["causal"])
+    assert name == fa.fa_query(128, fa.DTYPES["bf16"], fa.MASKS["causal"]) and grid == 32 * 32
+    # fewer work-groups than compute units: keys split over the waves
+    name, grid = fa.fa_query_fwd(2, 8, 8, 1024, 64, fa.DTYPES["bf16"], fa.MASKS["causal"])
+    assert "keysplit4" in name and "br64" in name and grid == 16 * 16
+    name, grid = fa.fa_query_fwd(1, 4, 2, 2000, 128, fa.DTYPES["f16"], fa.MASKS["window"], 300)
+    assert "keysplit2" in name and "br128" in name and grid == 4 * 16
+    # d = 256 and fp32 never split
+    assert "keysplit" not in fa.fa_query_fwd(1, 1, 1, 100, 256, 2, 0)[0]
+    assert fa.fa_query_fwd(1, 1, 1, 100, 64, 0, 0)[0].startswith("fa_fwd_f32")
+    for bad in ((0, 1, 1, 10, 64, 2, 0), (1, 3, 2, 10, 64, 2, 0), (1, 1, 1, 10, 64, 2, 2, 0)):
+        with pytest.raises(fa.FaError) as e:
+            fa.fa_query_fwd(*bad)
+        assert e.value.status == fa.FA_EINVAL
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_query_fwd(1, 1, 1, 10, 96, 2, 0)
     assert e.value.status == fa.FA_EUNSUPPORTED
 
 
