@@ -415,9 +415,23 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) s4a[h][j] = s4t[h][j] = -0.f;  // -0 + x == x folds away
   };
-  auto weight_unit = [&](int h, int kk, int j) __attribute__((always_inline)) {
-    const float p0 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j]);
-    const float p1 = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j + 1]);
+  // Weight units in step-major order: r -> (half (r/4) % NH, step r/(4 NH),
+  // pair r % 4); phase B makes r < UAB, phase A the rest.  Each unit runs in
+  // two stages: the exponentials of unit r are issued together with the pack
+  // and sums of unit r - 1 (w_exp(r), then w_fin(r - 1)), so that neither
+  // waits on the other's latency (a wave runs alone on its SIMD: nothing
+  // else hides an exponential's latency from the pack that reads it).
+  float pe[2][2];
+  auto w_exp = [&](int r) __attribute__((always_inline)) {
+    const int h = (r / 4) % NH, kk = r / (4 * NH), j = r % 4;
+    pe[r & 1][0] = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j]);
+    pe[r & 1][1] = __builtin_amdgcn_exp2f(xdef[h][kk][2 * j + 1]);
+    pin(pe[r & 1][0]);
+    pin(pe[r & 1][1]);
+  };
+  auto w_fin = [&](int r) __attribute__((always_inline)) {
+    const int h = (r / 4) % NH, kk = r / (4 * NH), j = r % 4;
+    const float p0 = pe[r & 1][0], p1 = pe[r & 1][1];
     pk[h][kk][j] = Ty::pack2(p0, p1);
     s4a[h][j] += p0 + p1;
     if constexpr (NK > 1) s4t[h][j] = Ty::add2(pk[h][kk][j], s4t[h][j]);
@@ -425,12 +439,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     pin(s4a[h][j]);
     if constexpr (NK > 1) pin(s4t[h][j]);
   };
-  // Weight units in step-major order: r -> (half (r/4) % NH, step r/(4 NH),
-  // pair r % 4); phase B makes r < UAB, phase A the rest.
-  auto b_weight_unit = [&](int r) __attribute__((always_inline)) {
-    weight_unit((r / 4) % NH, r / (4 * NH), r % 4);
+  auto a_unit = [&](int u) __attribute__((always_inline)) {
+    w_exp(u + UAB);
+    if (u > 0) w_fin(u - 1 + UAB);
   };
-  auto a_unit = [&](int u) __attribute__((always_inline)) { b_weight_unit(u + UAB); };
+  auto a_unit_last = [&]() __attribute__((always_inline)) { if (UA > 0) w_fin(UA - 1 + UAB); };
 
   // Offset update, off the common path.  The weights above were taken
   // against the current offset without looking at the tile's maximum.  A
@@ -478,15 +491,25 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       for (int db = 0; db < NDB; ++db) oacc[h][db] *= alpha;
     }
   };
-  auto a_finish = [&]() __attribute__((always_inline)) {
+  // `force` (the finish of the first tile) always takes the update: every row
+  // gets its offset there, except under a window, where a row's first
+  // visible key can lie in a later tile; `fresh` says that the finished tile
+  // may hold some of this wave's rows' first visible keys, and only then are
+  // rows without an offset looked for.
+  auto a_finish = [&](bool force, bool fresh) __attribute__((always_inline)) {
     bool trig = false;
+    uint64_t votes = 0;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       lpart[h] = (s4a[h][0] + s4a[h][1]) + (s4a[h][2] + s4a[h][3]);
+      votes |= __builtin_amdgcn_ballot_w64(lpart[h] > CAP);
       if constexpr (NK > 1) ltpart[h] = (s4t[h][0] + s4t[h][1]) + (s4t[h][2] + s4t[h][3]);
-      trig = trig || lpart[h] > CAP || m[h] == -INFINITY;
+
+      if (MASK == kMaskWindow && fresh) trig = trig || m[h] == -INFINITY;
     }
-    if (__any(trig)) settle();
+    if (force || votes != 0 ||
+        (MASK == kMaskWindow && fresh && __builtin_amdgcn_ballot_w64(trig) != 0))
+      settle();
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       l[h] += lpart[h];
@@ -514,8 +537,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 
   // One tile, software-pipelined (t = this tile):
   //   phase A: S(t) = K_t Q^T on MFMA, next to the remaining weight units of
-  //            tile t-1, its finish (offset test and the rare update) and
-  //            the direct loads of tile t+PF;
+  //            tile t-1, its finish (offset test and the rare update) under
+  //            the last few score MFMAs, the direct loads of tile t+PF, and
+  //            the first V operand reads of phase B;
   //   phase B: O += V_{t-1}^T P(t-1)^T on MFMA (both halves share each V
   //            operand), next to the argument units of tile t in its first
   //            half and tile t's first weight units in its second half,
@@ -532,7 +556,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   constexpr int UA_PRE = 1 < UA ? 1 : UA;        // units before the first MFMA
   // Tile with stage phase P = it % NST: K in stage P, the previous tile's V
   // in stage P-1, loads of tile it+PF into stage P+PF.
-  auto tile = [&](bool masked, auto phase_c, int k0, int lkt) __attribute__((always_inline)) {
+  auto tile = [&](bool masked, bool first, bool fresh, auto phase_c, int k0, int lkt)
+                  __attribute__((always_inline)) {
     constexpr int P = decltype(phase_c)::value;
     constexpr int kst = P, vprev = (P + NST - 1) % NST, lks = (P + PF) % NST, lvs = lks;
     const char *kl = (const char *)&k_lds[0][kst][0];
@@ -566,6 +591,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int u = 0; u < UA_PRE; ++u) a_unit(u);
     __builtin_amdgcn_sched_barrier(0);
+    u32x4 vop[RPD + 1];
+    // The finish of the previous tile runs after score MFMA FIN, so that the
+    // last score MFMAs (which it does not depend on) cover its vector work
+    // and branch, and the first V operands of phase B are read in the last
+    // RPD slots: the product phase then starts without waiting.
+    constexpr int FIN = MA - 4;
 #pragma unroll
     for (int st = 0; st < NSA; ++st) {
       if (st + RPD < NSA) kop[(st + RPD) % (RPD + 1)] = read_k(kl, st + RPD);
@@ -574,19 +605,26 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       for (int h = 0; h < NH; ++h) {
         const int mi = st * NH + h;
         sacc[h][kb] = Ty::mfma(kop[st % (RPD + 1)], qreg[h][ks], ks == 0 ? f32x16{} : sacc[h][kb]);
+        if (mi < FIN) {
 #pragma unroll
-        for (int u = UA_PRE + mi * (UA - UA_PRE) / MA; u < UA_PRE + (mi + 1) * (UA - UA_PRE) / MA; ++u)
-          a_unit(u);
+          for (int u = UA_PRE + mi * (UA - UA_PRE) / FIN; u < UA_PRE + (mi + 1) * (UA - UA_PRE) / FIN; ++u)
+            a_unit(u);
+        }
+        if (mi == FIN) {
+          a_unit_last();
+          a_finish(first, fresh);
+        }
+        if (mi >= MA - RPD) vop[mi - (MA - RPD)] = read_v(vl, mi - (MA - RPD));
 #pragma unroll
         for (int d = 0; d < NDMA; ++d)
           if (dma_slot(d) == mi) dma(d);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    a_finish();
-    u32x4 vop[RPD + 1];
-#pragma unroll
-    for (int st = 0; st < RPD && st < NSB; ++st) vop[st] = read_v(vl, st);
+    if (FIN >= MA) {
+      a_unit_last();
+      a_finish(first, fresh);
+    }
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase B ----
     if (masked) apply_mask(k0);  // per-wave scalar branch at a fence point
@@ -605,11 +643,15 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
         } else {
           const int q = mi - MB / 2;
 #pragma unroll
-          for (int r = q * UAB / (MB / 2); r < (q + 1) * UAB / (MB / 2); ++r) b_weight_unit(r);
+          for (int r = q * UAB / (MB / 2); r < (q + 1) * UAB / (MB / 2); ++r) {
+            w_exp(r);
+            if (r > 0) w_fin(r - 1);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if (UAB > 0) w_fin(UAB - 1);
   };
 
   // Zero the V stage that the first tile's (empty) pending product reads, so
@@ -654,6 +696,16 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // factor 1).
   const int n_steps = (kt_end - kt_begin + NK - 1) / NK;
   const int n_pad = (n_steps + NST - 1) / NST * NST;
+  // Under a window, whether tile kt (of this wave's key group) can hold the
+  // first key of some row of this wave that the group sees: rows wr0..wr1
+  // first see keys wr0 - W + 1 .. wr1 - W + 1, and a key group's first tile
+  // at or after such a key starts at most NK - 1 tiles after the tile that
+  // holds it.
+  auto fresh_window = [&](int kt) __attribute__((always_inline)) {
+    if (MASK != kMaskWindow) return false;
+    const int k0 = kt * BC;
+    return k0 + BC - 1 >= wr0 - a.window + 1 && k0 <= wr1 - a.window + 1 + (NK - 1) * BC;
+  };
   auto need_mask = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BC;
     if (kt >= kt_end) return true;
@@ -668,7 +720,10 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // here may be overwritten.
   auto step = [&](auto phase_c, int it) __attribute__((always_inline)) {
     const int kt = tile_of(it);
-    tile(need_mask(kt), phase_c, kt * BC, tile_or_none(tile_of(it + PF)));
+    // (the finish in step `it` is that of tile_of(it - 1); the first tile's
+    // always takes the offset update)
+    tile(need_mask(kt), it <= 1, fresh_window(tile_of(it - 1)), phase_c, kt * BC,
+         tile_or_none(tile_of(it + PF)));
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
     __builtin_amdgcn_s_barrier();
   };
@@ -681,7 +736,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // The last tile: its remaining weights, then its PV products.
 #pragma unroll
   for (int u = 0; u < UA; ++u) a_unit(u);
-  a_finish();
+  a_unit_last();
+  a_finish(n_pad <= 1, fresh_window(tile_of(n_pad - 1)));
   if (n_pad > 0) o_phase(NST - 1);
 
   // Row statistics of the rows this wave holds: offset m (base 2) and the
