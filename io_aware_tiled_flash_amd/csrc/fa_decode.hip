@@ -42,22 +42,10 @@ constexpr int kThreads = 256;
 constexpr int kMaxSplitLen = 4096;               // tokens per work-group at most
 constexpr int kMaxTable = kMaxSplitLen + 2;      // table entries one split can touch
 constexpr float kTau = 8.f;                      // lazy-rescale threshold (base 2)
-#ifndef FA_DEC_MFMA_ROWS
-#define FA_DEC_MFMA_ROWS 5
-#endif
-constexpr int kMfmaRows = FA_DEC_MFMA_ROWS;      // query rows per key/value head for MFMA
-#ifndef FA_DEC_MFMA_GROUPS
-#define FA_DEC_MFMA_GROUPS 1024
-#endif
-constexpr int kMfmaGroups = FA_DEC_MFMA_GROUPS;  // work-groups the MFMA path aims for
-#ifndef FA_DEC_VALU_GROUPS
-#define FA_DEC_VALU_GROUPS 4096
-#endif
-constexpr int kValuGroups = FA_DEC_VALU_GROUPS;  // work-groups the vector path aims for
-#ifndef FA_DEC_MIN_SPLIT
-#define FA_DEC_MIN_SPLIT 1024
-#endif
-constexpr int kMinSplit = FA_DEC_MIN_SPLIT;      // shortest split worth its merge
+constexpr int kMfmaRows = 5;                     // query rows per key/value head for MFMA
+constexpr int kMfmaGroups = 1024;                // work-groups the MFMA path aims for
+constexpr int kValuGroups = 4096;                // work-groups the vector path aims for
+constexpr int kMinSplit = 1024;                  // shortest split worth its merge
 
 
 template <class Ty> struct Dot;
@@ -278,9 +266,17 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeArgs a)
   }
 }
 
-// Combine the splits of every output row whose request needed more than one.
+// Combine the splits of every output row whose request needed more than one:
+// LSE = log sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.  One wave per
+// row; the partials are hot in L2, so the kernel is latency-bound: the
+// splits' logsumexps are read by all lanes at once (lane s: split s, then
+// s + 64, ...) and reduced across the wave, and the partial rows are read
+// eight splits at a time (each lane D/64 columns) before they are combined,
+// in split order.
 template <class Ty, int D>
 __global__ __launch_bounds__(kThreads) void fa_decode_merge_kernel(DecodeArgs a) {
+  constexpr int CPL = D / 64;  // output columns per lane
+  constexpr int U = 8;         // splits whose partial rows are in flight together
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= a.B * a.H * a.n_q) return;
@@ -291,23 +287,42 @@ __global__ __launch_bounds__(kThreads) void fa_decode_merge_kernel(DecodeArgs a)
   const float *ls = a.ws_lse + (size_t)row * a.n_splits;
   const float *os = a.ws_o + (size_t)row * a.n_splits * D;
   float mx = -INFINITY;
-  for (int s = 0; s < ns_b; ++s) mx = fmaxf(mx, ls[s]);
+  for (int s = lane; s < ns_b; s += 64) mx = fmaxf(mx, ls[s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   uint16_t *orow = (uint16_t *)a.o + (size_t)row * D;
   if (mx == -INFINITY) {
-    for (int e = lane; e < D; e += 64) orow[e] = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) orow[lane + 64 * c] = 0;
     if (lane == 0) a.lse[row] = -INFINITY;
     return;
   }
   constexpr float kLog2e = 1.4426950408889634f;
   float sum = 0.f;
-  for (int s = 0; s < ns_b; ++s) sum += __builtin_amdgcn_exp2f((ls[s] - mx) * kLog2e);
+  for (int s = lane; s < ns_b; s += 64) sum += __builtin_amdgcn_exp2f((ls[s] - mx) * kLog2e);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
   const float lse = mx + __builtin_amdgcn_logf(sum) * 0.69314718055994531f;
-  for (int e = lane; e < D; e += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < ns_b; ++s)
-      acc = fmaf(__builtin_amdgcn_exp2f((ls[s] - lse) * kLog2e), os[(size_t)s * D + e], acc);
-    orow[e] = (uint16_t)(Ty::pack2(acc, 0.f) & 0xffffu);
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int s0 = 0; s0 < ns_b; s0 += U) {
+    float w[U], v[U][CPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // past the last split: re-read the last one (a valid address) with weight 0
+      const int s = min(s0 + u, ns_b - 1);
+      w[u] = s0 + u < ns_b ? __builtin_amdgcn_exp2f((ls[s] - lse) * kLog2e) : 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[u][c] = os[(size_t)s * D + lane + 64 * c];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w[u], v[u][c], acc[c]);
   }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) orow[lane + 64 * c] = (uint16_t)(Ty::pack2(acc[c], 0.f) & 0xffffu);
   if (lane == 0) a.lse[row] = lse;
 }
 
@@ -350,13 +365,7 @@ template <> struct M16<TF16> {
 // instructions covers 64 bytes of 16 rows, and the rows' other bytes follow
 // in the next instructions (measured 2.86 against 2.67 TB/s with
 // non-temporal loads at 16 rows per key/value head).
-#ifndef FA_DEC_M16_NT
-#define FA_DEC_M16_NT 0
-#endif
-__device__ inline u32x4 m16_load(const u32x4 *p) {
-  if (FA_DEC_M16_NT) return __builtin_nontemporal_load(p);
-  return *p;
-}
+__device__ inline u32x4 m16_load(const u32x4 *p) { return *p; }
 
 template <class Ty, int D>
 __global__ __launch_bounds__(kThreads, 3) void fa_decode_m16_kernel(DecodeArgs a) {
