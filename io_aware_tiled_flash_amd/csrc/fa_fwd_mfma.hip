@@ -106,6 +106,15 @@ __device__ inline void load16_to_lds_s(u32x4 rsrc, uint32_t byte_off, uint32_t l
       : "memory");
 }
 
+// f(stage phase P, it + P) for P = P0 .. N-1, each with a compile-time phase.
+template <int P0, int N, class F>
+__device__ inline __attribute__((always_inline)) void unroll_steps(F &f, int it) {
+  if constexpr (P0 < N) {
+    f(std::integral_constant<int, P0>{}, it + P0);
+    unroll_steps<P0 + 1, N>(f, it);
+  }
+}
+
 // Offset-move cap: a lane's tile weight sum above it sends the wave to the
 // offset update.  bf16 weights share fp32's exponent range, so they may grow
 // to 2^32 before the offset has to move (the accumulator then stays below
@@ -140,7 +149,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // NST times, which makes every stage offset a compile-time immediate of the
   // LDS instructions.
   constexpr int NST = PF + 2;
-  static_assert(NST == 4, "the tile loop below is unrolled four times");
   constexpr int NVST = NST;
   constexpr int LOADS_PER_TILE = 2 * LOADS_PER_WAVE;  // per wave, K and V
   static_assert(LOADS_PER_TILE * (PF - 1) < 64, "vmcnt range");
@@ -682,12 +690,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   asm volatile("" ::"s"(rk), "s"(rv), "s"(a.o), "s"(a.lse));
 
   // The work-group's steps run in groups of NST, each copy of the tile with
-  // its own compile-time stage phase.  Every key group takes the same number
-  // of steps (the largest group's share, padded to a multiple of NST) with
-  // tiles past the last visible one: their loads read the out-of-range index
-  // (zero fill) and all their scores are masked, so they contribute weight 0
-  // and factor 1 (none for the 256-row work-groups of a causal sequence,
-  // whose visible range is a multiple of 4 tiles).
+  // its own compile-time stage phase; the loop leaves at the first step past
+  // the last one (a scalar branch per step).  Every key group takes the same
+  // number of steps (the largest group's share, so the barriers match), a
+  // group with fewer tiles finishing with one past its last visible one: its
+  // loads read the out-of-range index (zero fill) and all its scores are
+  // masked, so it contributes weight 0 and factor 1.
   //
   // Every wave of a key group runs every tile of that group (the loads are
   // shared within the group, the barriers by all).  A wave masks a tile
@@ -695,7 +703,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // outside it; a tile outside the band is simply fully masked (weights 0,
   // factor 1).
   const int n_steps = (kt_end - kt_begin + NK - 1) / NK;
-  const int n_pad = (n_steps + NST - 1) / NST * NST;
   // Under a window, whether tile kt (of this wave's key group) can hold the
   // first key of some row of this wave that the group sees: rows wr0..wr1
   // first see keys wr0 - W + 1 .. wr1 - W + 1, and a key group's first tile
@@ -720,25 +727,26 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // here may be overwritten.
   auto step = [&](auto phase_c, int it) __attribute__((always_inline)) {
     const int kt = tile_of(it);
-    // (the finish in step `it` is that of tile_of(it - 1); the first tile's
-    // always takes the offset update)
-    tile(need_mask(kt), it <= 1, fresh_window(tile_of(it - 1)), phase_c, kt * BC,
+    // (the finish in step `it` is that of tile_of(it - 1), none in step 0;
+    // the first tile's always takes the offset update)
+    tile(need_mask(kt), it == 1, it > 0 && fresh_window(tile_of(it - 1)), phase_c, kt * BC,
          tile_or_none(tile_of(it + PF)));
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
     __builtin_amdgcn_s_barrier();
   };
-  for (int it = 0; it < n_pad; it += NST) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
-    step(std::integral_constant<int, 2>{}, it + 2);
-    step(std::integral_constant<int, 3>{}, it + 3);
-  }
-  // The last tile: its remaining weights, then its PV products.
+  auto step_if = [&](auto phase_c, int it) __attribute__((always_inline)) {
+    if (it < n_steps) step(phase_c, it);
+  };
+  for (int it = 0; it < n_steps; it += NST) unroll_steps<0, NST>(step_if, it);
+  // The last tile: its remaining weights, then its PV products (its V stage
+  // is that of step n_steps - 1).
 #pragma unroll
   for (int u = 0; u < UA; ++u) a_unit(u);
   a_unit_last();
-  a_finish(n_pad <= 1, fresh_window(tile_of(n_pad - 1)));
-  if (n_pad > 0) o_phase(NST - 1);
+  a_finish(n_steps == 1, fresh_window(tile_of(n_steps - 1)));
+  if (n_steps > 0) o_phase((n_steps - 1) % NST);
+  // Zero-fill loads issued past the last tile may still be writing LDS.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Row statistics of the rows this wave holds: offset m (base 2) and the
   // full denominators (both lanes of a row).
@@ -755,8 +763,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     // O = sum O_g 2^(m_g - m) (a group that saw no visible key of a row has
     // m_g = -inf and factor 0).  The stages are reused for the partials
     // (accumulators in the K stages, row statistics in the V stages) once
-    // every wave is done with them and the zero-fill loads still in flight
-    // (past the last tile) have landed.  The partials are stored in the
+    // every wave is done with them (the zero-fill loads past the last tile
+    // have landed: see the wait above).  The partials are stored in the
     // register layout (16 bytes per lane, consecutive lanes), so the stores
     // and reads are conflict-free.
     constexpr int NBLK = NH * NDB;                       // accumulator blocks per wave
@@ -765,7 +773,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     static_assert((NK - 1) * NR * NH * 1024 <= (int)sizeof(v_lds), "merge space (statistics)");
     char *mbuf = (char *)&k_lds[0][0][0];
     char *sbuf = (char *)&v_lds[0][0][0];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     if (kg > 0) {
       const int p0 = (kg - 1) * NR + rg;
