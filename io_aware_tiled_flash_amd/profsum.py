@@ -169,7 +169,11 @@ def cmd_sq(a) -> list[str]:
         out.append(f"  dispatch_ns (counter runs, mean): {dur_ns:.0f}")
     if "GRBM_GUI_ACTIVE" in vals and dur_ns:
         ghz = vals["GRBM_GUI_ACTIVE"] / N_XCD / dur_ns
-        out.append(f"  clock_GHz (GRBM_GUI_ACTIVE / 8 dies / dispatch time): {ghz:.3f}")
+        note = ""
+        if dur_ns < 100e3:
+            note = ("  (not a clock: for a dispatch this short the GPU-busy count covers"
+                    " more than the kernel's own span)")
+        out.append(f"  clock_GHz (GRBM_GUI_ACTIVE / 8 dies / dispatch time): {ghz:.3f}{note}")
     flops = w.flops()
     if "SQ_INSTS_MFMA" in vals:
         mf = vals["SQ_INSTS_MFMA"]
