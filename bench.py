@@ -15,7 +15,10 @@ mean, median and minimum step times are all reported), bracketed by
 synchronisation.  A shader-clock sample taken on the same stream right
 before and right after the timed steps gives the mean clock over them, and
 the line quotes the percentage of peak both against the published peak
-(2.4 GHz) and against the peak at that measured clock.
+(2.4 GHz) and against the peak at that measured clock.  After the timed steps
+a matrix-core ceiling run (``mfma_ceiling``; ``--no-ceiling`` skips it)
+measures what the MFMA units sustain on operands like the inputs with
+nothing else to do, and the line also gives the kernel's fraction of that.
 
 Prints one JSON line: the headline metric (forward TFLOP/s, causal FLOPs
 counted as 4*d per visible pair) plus a ``roofline`` object for the kernel and
@@ -44,6 +47,9 @@ HBM_PEAK_GBS = 8000.0
 # dP recomputed once, dV, dK, dQ) against the forward's two, the usual
 # accounting; recomputing S and dP a second time for dQ is not counted.
 BWD_FLOP_RATIO = 2.5
+# The backward's kernels issue 14*d FLOPs per visible pair (the dK/dV kernel
+# recomputes S and dP, and so does the dQ kernel): 1.4 times the credited 10*d.
+BWD_ISSUED_RATIO = 1.4
 BWD_KERNELS = ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel")
 GRAD_SEED_OFFSET = 7919  # dO is drawn with seed = the workload's seed + this
 DECODE_DEFAULT = "decode_opt13b_b256"
@@ -165,6 +171,62 @@ class ClockSampler:
                                 for d_, v_ in sorted(dies.items())},
                 "method": "per compute unit: shader-cycle counter over the real-time counter, "
                           "sampled on the launch stream right before and after the timed steps"}
+
+
+def mfma_ceiling(device, stream, dtype: str, clock: "ClockSampler", launch_s: float = 0.25,
+                 settle_s: float = 1.0):
+    """Sustained matrix-core rate of this part on operands like the inputs
+    (roughly standard normal bf16 or fp16), with nothing else in the loop
+    (libfa_clock.so, measurement support): launches of 32 x 32 x 16 MFMA
+    chains run for about settle_s, then two launches are timed between
+    events, with a clock sample on either side.  Under sustained load the
+    power limit sets the clock, so no kernel on such operands can beat this
+    rate; the attention kernels are also quoted as a fraction of it."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "io_aware_tiled_flash_amd", "libfa_clock.so"))
+    lib.fa_mfma_ceiling.restype = ctypes.c_int
+    lib.fa_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_uint, ctypes.c_void_p]
+    code = {"f16": 1, "bf16": 2}[dtype]
+    n_wg = 8192  # 32 per compute unit: the tail of the last round is small
+    out = torch.empty(256 * n_wg, dtype=torch.float32, device=device)
+
+    def launch(rounds):
+        st = lib.fa_mfma_ceiling(out.data_ptr(), n_wg, rounds, code, 12345, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"MFMA ceiling launch failed ({st})")
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    with torch.cuda.stream(stream):
+        ev[0].record(stream)
+        launch(64)
+        ev[1].record(stream)
+        stream.synchronize()
+        ms = ev[0].elapsed_time(ev[1])
+        rounds = max(64, int(64 * launch_s * 1e3 / max(ms, 1e-3)))
+        t0 = time.time()
+        while time.time() - t0 < settle_s:
+            launch(rounds)
+            stream.synchronize()
+        clock.sample(0)
+        ev[0].record(stream)
+        launch(rounds)
+        launch(rounds)
+        ev[1].record(stream)
+        clock.sample(1)
+        stream.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    flop = 2.0 * n_wg * 4 * rounds * 64 * 32768
+    tflops = flop / (ms * 1e-3) / 1e12
+    clk = clock.mean_mhz()
+    return {"TFLOP/s": round(tflops, 1),
+            "frac_of_published_peak": round(tflops / PEAK_TFLOPS[dtype], 4),
+            "clock_MHz": clk["mean_MHz"] if clk else None,
+            "seconds_timed": round(ms * 1e-3, 3), "settle_s": settle_s,
+            "method": "v_mfma_f32_32x32x16 chains on register operands drawn about standard "
+                      "normal, 4 independent accumulators per wave, no memory traffic"}
 
 
 def time_steps(step, stream, steps: int, warmup: int, settle_s: float, clock=None):
@@ -406,6 +468,9 @@ def main() -> int:
                          "paged-cache decoding (workload default: " + DECODE_DEFAULT + ")")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
+                    help="skip the matrix-core ceiling run (about 1.5 s) that the forward and "
+                         "backward lines are also quoted against")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this "
                          "many MiB per step (reference for HBM byte counters)")
@@ -519,6 +584,12 @@ def main() -> int:
         result["roofline"]["frac_at_measured_clock"] = round(tflops / peak_at, 4)
     if bwd:
         result["roofline"]["scope"] = "whole pass (three launches)"
+        result["roofline"]["mfma_flop_issued_per_credited"] = BWD_ISSUED_RATIO
+    if args.ceiling and w.dtype in ("bf16", "f16"):
+        ceil = mfma_ceiling(dev, stream, w.dtype, clock)
+        result["mfma_ceiling"] = ceil
+        issued = tflops * (BWD_ISSUED_RATIO if bwd else 1.0)
+        result["roofline"]["frac_of_mfma_ceiling"] = round(issued / ceil["TFLOP/s"], 4)
     if args.cpu_seconds > 0:
         if bwd:
             result["cpu_baseline"] = cpu_baseline_bwd(w, *host, dout.cpu(), args.cpu_seconds)
