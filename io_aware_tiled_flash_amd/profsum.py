@@ -100,6 +100,10 @@ def cmd_trace(a) -> list[str]:
                        f"{sum(last) / len(last):.0f}")
             out.append(f"  median_ns_last_{a.last}_calls: {statistics.median(last):.0f}")
             out.append(f"  min_ns_last_{a.last}_calls: {min(last)}")
+    sys.path.insert(0, ROOT)
+    import bench
+    out.append(f"kernel_source_digest: {bench.kernel_source_digest(tuple(a.sources))}"
+               f"  ({' '.join(a.sources)})")
     return out
 
 
@@ -217,6 +221,8 @@ def main(argv=None) -> int:
     t.add_argument("--dir", required=True)
     t.add_argument("--workload", required=True)
     t.add_argument("--last", type=int, default=0)
+    t.add_argument("--sources", nargs="+",
+                   default=["fa_fwd_mfma.hip", "fa_gfx950.h", "fa_internal.h"])
     t.add_argument("--cmd", action="append", default=[])
     f = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
