@@ -41,7 +41,8 @@
 //     the wave issues it;
 //   * tiles are loaded PF tiles ahead of the math into free LDS stages (PF+1
 //     for K, PF+2 for V because the PV products lag one tile), which hides
-//     the L2/HBM latency behind several tiles of math; one barrier per tile;
+//     the L2/HBM latency behind several tiles of math; one barrier per tile
+//     (none when each key group of a key-split instance is one wave);
 //   * causal and sliding-window masks skip whole tiles: the work-group visits
 //     only key tiles that intersect its rows' visible band, and the
 //     elementwise mask (scores set to -inf) runs only on tiles that straddle
@@ -698,7 +699,10 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // masked, so it contributes weight 0 and factor 1.
   //
   // Every wave of a key group runs every tile of that group (the loads are
-  // shared within the group, the barriers by all).  A wave masks a tile
+  // shared within the group; every wave takes the same number of steps).
+  // When a key group is a single wave (NR = 1), no other wave reads or
+  // writes its stages, so its own load-counter wait is all a step needs and
+  // the waves run without a barrier until the merge.  A wave masks a tile
   // elementwise when the tile straddles an edge of its rows' band or lies
   // outside it; a tile outside the band is simply fully masked (weights 0,
   // factor 1).
@@ -732,7 +736,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     tile(need_mask(kt), it == 1, it > 0 && fresh_window(tile_of(it - 1)), phase_c, kt * BC,
          tile_or_none(tile_of(it + PF)));
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
-    __builtin_amdgcn_s_barrier();
+    if constexpr (NR > 1) __builtin_amdgcn_s_barrier();
   };
   auto step_if = [&](auto phase_c, int it) __attribute__((always_inline)) {
     if (it < n_steps) step(phase_c, it);
