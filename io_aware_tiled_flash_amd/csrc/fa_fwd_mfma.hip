@@ -762,51 +762,58 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   }
 
   if constexpr (NK > 1) {
-    // Merge of the key groups' partial results, row group by row group, in
-    // key group 0's waves: m = max m_g, l = sum l_g 2^(m_g - m),
-    // O = sum O_g 2^(m_g - m) (a group that saw no visible key of a row has
-    // m_g = -inf and factor 0).  The stages are reused for the partials
-    // (accumulators in the K stages, row statistics in the V stages) once
-    // every wave is done with them (the zero-fill loads past the last tile
-    // have landed: see the wait above).  The partials are stored in the
-    // register layout (16 bytes per lane, consecutive lanes), so the stores
-    // and reads are conflict-free.
-    constexpr int NBLK = NH * NDB;                       // accumulator blocks per wave
-    constexpr int O_BYTES = (NK - 1) * NR * NBLK * 4096;  // 16 floats x 64 lanes each
-    static_assert(O_BYTES <= (int)sizeof(k_lds), "merge space (accumulators)");
-    static_assert((NK - 1) * NR * NH * 1024 <= (int)sizeof(v_lds), "merge space (statistics)");
+    // Merge of the key groups' partial results: m = max m_g,
+    // l = sum l_g 2^(m_g - m), O = sum O_g 2^(m_g - m) (a group that saw no
+    // visible key of a row has m_g = -inf and factor 0).  The work is shared
+    // out by accumulator block: block b = h * NDB + db of a row group is
+    // merged, normalised and stored by key group b % NK, which reads the
+    // other groups' partials of that block from LDS.  Every wave writes the
+    // blocks it hands on and its row statistics, then all waves merge at once.
+    // The stages are reused for the partials (accumulators in the K stages,
+    // row statistics in the V stages) once every wave is done with them (the
+    // zero-fill loads past the last tile have landed: see the wait above).
+    // The partials are stored in the register layout (16 bytes per lane,
+    // consecutive lanes), so the stores and reads are conflict-free.  The
+    // terms are summed in key-group order whichever group merges, so the
+    // result does not depend on which wave does it.
+    constexpr int NBLK = NH * NDB;      // accumulator blocks per wave
+    constexpr int NOUT = NBLK - NBLK / NK;  // blocks a wave hands to other groups
+    static_assert(NBLK % NK == 0, "blocks must split evenly over the key groups");
+    static_assert(NW * NOUT * 4096 <= (int)sizeof(k_lds), "merge space (accumulators)");
+    static_assert(NW * NH * 1024 <= (int)sizeof(v_lds), "merge space (statistics)");
     char *mbuf = (char *)&k_lds[0][0][0];
     char *sbuf = (char *)&v_lds[0][0][0];
+    // byte offset of block b as written by key group g of this row group
+    // (a group writes the blocks of the other groups, in block order)
+    auto slot = [&](int g, int b) __attribute__((always_inline)) {
+      const int j = (b / NK) * (NK - 1) + (b % NK) - (b % NK > g ? 1 : 0);
+      return ((g * NR + rg) * NOUT + j) * 4096;
+    };
     __builtin_amdgcn_s_barrier();
-    if (kg > 0) {
-      const int p0 = (kg - 1) * NR + rg;
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
+    for (int h = 0; h < NH; ++h) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db) {
+        const int bl = h * NDB + db;
+        if (bl % NK == kg) continue;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x16 &o = oacc[h][db];
-            *(f32x4 *)(mbuf + (p0 * NBLK + h * NDB + db) * 4096 + (j * 64 + lane) * 16) =
-                f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
-          }
-        *(f32x4 *)(sbuf + ((p0 * NH + h) * 64 + lane) * 16) =
-            f32x4{m[h], l_tot[h], lt_tot[h], 0.f};
+        for (int j = 0; j < 4; ++j) {
+          const f32x16 &o = oacc[h][db];
+          *(f32x4 *)(mbuf + slot(kg, bl) + (j * 64 + lane) * 16) =
+              f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
+        }
       }
+      *(f32x4 *)(sbuf + (((kg * NR + rg) * NH + h) * 64 + lane) * 16) =
+          f32x4{m[h], l_tot[h], lt_tot[h], 0.f};
     }
     __builtin_amdgcn_s_barrier();
-    if (kg > 0) return;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       float mg[NK], lgs[NK], ltg[NK];
-      mg[0] = m[h];
-      lgs[0] = l_tot[h];
-      ltg[0] = lt_tot[h];
-      float mm = m[h];
+      float mm = -INFINITY;
 #pragma unroll
-      for (int g = 1; g < NK; ++g) {
-        const f32x4 ml =
-            *(const f32x4 *)(sbuf + ((((g - 1) * NR + rg) * NH + h) * 64 + lane) * 16);
+      for (int g = 0; g < NK; ++g) {
+        const f32x4 ml = *(const f32x4 *)(sbuf + (((g * NR + rg) * NH + h) * 64 + lane) * 16);
         mg[g] = ml[0];
         lgs[g] = ml[1];
         ltg[g] = ml[2];
@@ -821,16 +828,22 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        f32x16 acc = oacc[h][db] * f[0];
+        const int bl = h * NDB + db;
+        if (bl % NK != kg) continue;
+        f32x16 acc;
 #pragma unroll
-        for (int g = 1; g < NK; ++g) {
-          const int p = (g - 1) * NR + rg;
+        for (int g = 0; g < NK; ++g) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const f32x4 o =
-                *(const f32x4 *)(mbuf + (p * NBLK + h * NDB + db) * 4096 + (j * 64 + lane) * 16);
+            f32x4 o;
+            if (g == kg)
+              o = f32x4{oacc[h][db][4 * j], oacc[h][db][4 * j + 1], oacc[h][db][4 * j + 2],
+                        oacc[h][db][4 * j + 3]};
+            else
+              o = *(const f32x4 *)(mbuf + slot(g, bl) + (j * 64 + lane) * 16);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[4 * j + e] = fmaf(f[g], o[e], acc[4 * j + e]);
+            for (int e = 0; e < 4; ++e)
+              acc[4 * j + e] = g == 0 ? o[e] * f[0] : fmaf(f[g], o[e], acc[4 * j + e]);
           }
         }
         oacc[h][db] = acc;
@@ -841,7 +854,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     }
   }
 
-  // Epilogue: one division per row, RNE to the element type, natural-log LSE.
+  // Epilogue: one division per row, RNE to the element type, natural-log LSE
+  // (under a key split, each key group stores the blocks it merged, and the
+  // group holding a half's first block its LSE).
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int row = wr0 + 32 * h + lq;
@@ -850,6 +865,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
       uint16_t *orow = (uint16_t *)a.o + head_off + (size_t)row * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
+        if (NK > 1 && (h * NDB + db) % NK != kg) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           u32x2 w;
@@ -858,7 +874,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
           *(u32x2 *)(orow + 32 * db + 8 * j + 4 * lg) = w;
         }
       }
-      if (lg == 0)
+      if (lg == 0 && (NK == 1 || (h * NDB) % NK == kg))
         a.lse[(size_t)bh * S + row] =
             (m[h] + __builtin_amdgcn_logf(l_tot[h])) * 0.69314718055994531f;
     }
