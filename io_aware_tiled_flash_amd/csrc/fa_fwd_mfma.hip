@@ -605,7 +605,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     // last score MFMAs (which it does not depend on) cover its vector work
     // and branch, and the first V operands of phase B are read in the last
     // RPD slots: the product phase then starts without waiting.
-    constexpr int FIN = MA - 4;
+    // (with fewer than 8 score MFMAs, after the first half of them)
+    constexpr int FIN = MA >= 8 ? MA - 4 : MA / 2;
+    static_assert(FIN >= 1 || UA <= UA_PRE, "weight units need score MFMAs before the finish");
 #pragma unroll
     for (int st = 0; st < NSA; ++st) {
       if (st + RPD < NSA) kop[(st + RPD) % (RPD + 1)] = read_k(kl, st + RPD);
@@ -777,8 +779,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     // terms are summed in key-group order whichever group merges, so the
     // result does not depend on which wave does it.
     constexpr int NBLK = NH * NDB;      // accumulator blocks per wave
-    constexpr int NOUT = NBLK - NBLK / NK;  // blocks a wave hands to other groups
-    static_assert(NBLK % NK == 0, "blocks must split evenly over the key groups");
+    // With fewer blocks than key groups, groups NBLK.. merge nothing and
+    // every block has a slot of its own per writer; otherwise a group writes
+    // only the other groups' blocks, packed.
+    constexpr bool SPARSE = NBLK % NK != 0;
+    constexpr int NOUT = SPARSE ? NBLK : NBLK - NBLK / NK;  // slots per writing wave
+    static_assert(!SPARSE || NBLK < NK, "blocks must split evenly over the key groups");
     static_assert(NW * NOUT * 4096 <= (int)sizeof(k_lds), "merge space (accumulators)");
     static_assert(NW * NH * 1024 <= (int)sizeof(v_lds), "merge space (statistics)");
     char *mbuf = (char *)&k_lds[0][0][0];
@@ -786,7 +792,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     // byte offset of block b as written by key group g of this row group
     // (a group writes the blocks of the other groups, in block order)
     auto slot = [&](int g, int b) __attribute__((always_inline)) {
-      const int j = (b / NK) * (NK - 1) + (b % NK) - (b % NK > g ? 1 : 0);
+      const int j = SPARSE ? b : (b / NK) * (NK - 1) + (b % NK) - (b % NK > g ? 1 : 0);
       return ((g * NR + rg) * NOUT + j) * 4096;
     };
     __builtin_amdgcn_s_barrier();
@@ -887,9 +893,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 // the key groups, for grids too small to fill the chip.
 template <class Ty, int D, int MASK, int NK>
 struct Instance {
-  static constexpr int NW = 4;
+  // d = 64 key splits: 8 waves of 32 rows, two per key group and two per
+  // SIMD (169 registers), so that a step's softmax work is split over twice
+  // the waves; everything else: 4 waves, one per SIMD.
+  static constexpr int NW = (D == 64 && NK > 1) ? 8 : 4;
   static constexpr int BC = NK > 1 ? 32 : D == 64 ? 64 : 32;  // keys per tile
-  static constexpr int NH = D <= 128 ? 2 : 1;
+  static constexpr int NH = (D == 64 && NK > 1) ? 1 : D <= 128 ? 2 : 1;
   static constexpr int PF = 2;
   static constexpr int BR = 32 * NH * (NW / NK);
   static bool run(const FwdArgs *a, hipStream_t stream, bool launch, LaunchInfo *info,
