@@ -893,12 +893,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
 // the key groups, for grids too small to fill the chip.
 template <class Ty, int D, int MASK, int NK>
 struct Instance {
-  // d = 64 key splits: 8 waves of 32 rows, two per key group and two per
-  // SIMD (169 registers), so that a step's softmax work is split over twice
-  // the waves; everything else: 4 waves, one per SIMD.
-  static constexpr int NW = (D == 64 && NK > 1) ? 8 : 4;
+  // Key splits (d <= 128): 8 waves of 32 rows, two per SIMD (169 registers
+  // at d = 64, about 200 at d = 128), so that a step's softmax work is split
+  // over twice the waves; everything else: 4 waves, one per SIMD.
+  static constexpr int NW = (D <= 128 && NK > 1) ? 8 : 4;
   static constexpr int BC = NK > 1 ? 32 : D == 64 ? 64 : 32;  // keys per tile
-  static constexpr int NH = (D == 64 && NK > 1) ? 1 : D <= 128 ? 2 : 1;
+  static constexpr int NH = (D <= 128 && NK > 1) ? 1 : D <= 128 ? 2 : 1;
   static constexpr int PF = 2;
   static constexpr int BR = 32 * NH * (NW / NK);
   static bool run(const FwdArgs *a, hipStream_t stream, bool launch, LaunchInfo *info,
