@@ -731,26 +731,44 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // barrier extends that to the whole work-group.  Every LDS read of this
   // tile was consumed by an MFMA above, so after the barrier the stages read
   // here may be overwritten.
+  // Steps 0 .. it_hi hold the tiles this wave can see any key of.  Under a
+  // causal or window mask the tiles after it (keys past the wave's last row)
+  // it only loads for (its share of the work-group's tiles) and synchronises
+  // on: no MFMA, no softmax.  Every wave still takes n_steps steps, so the
+  // barriers match.  Under a key split every wave runs every step.
+  int it_hi = n_steps - 1;
+  if (NK == 1 && MASK != kMaskNone) it_hi = min(it_hi, min(wr1, S - 1) / BC - kt_begin);
+  auto sync = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
+    if constexpr (NR > 1) __builtin_amdgcn_s_barrier();
+  };
   auto step = [&](auto phase_c, int it) __attribute__((always_inline)) {
     const int kt = tile_of(it);
     // (the finish in step `it` is that of tile_of(it - 1), none in step 0;
     // the first tile's always takes the offset update)
     tile(need_mask(kt), it == 1, it > 0 && fresh_window(tile_of(it - 1)), phase_c, kt * BC,
          tile_or_none(tile_of(it + PF)));
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
-    if constexpr (NR > 1) __builtin_amdgcn_s_barrier();
+    sync();
   };
   auto step_if = [&](auto phase_c, int it) __attribute__((always_inline)) {
-    if (it < n_steps) step(phase_c, it);
+    if (it <= it_hi) step(phase_c, it);
   };
-  for (int it = 0; it < n_steps; it += NST) unroll_steps<0, NST>(step_if, it);
-  // The last tile: its remaining weights, then its PV products (its V stage
-  // is that of step n_steps - 1).
+  for (int it = 0; it <= it_hi; it += NST) unroll_steps<0, NST>(step_if, it);
+  // The last visible tile: its remaining weights, then its PV products (its
+  // V stage is that of step it_hi).
+  if (it_hi >= 0) {
 #pragma unroll
-  for (int u = 0; u < UA; ++u) a_unit(u);
-  a_unit_last();
-  a_finish(n_steps == 1, fresh_window(tile_of(n_steps - 1)));
-  if (n_steps > 0) o_phase((n_steps - 1) % NST);
+    for (int u = 0; u < UA; ++u) a_unit(u);
+    a_unit_last();
+    a_finish(it_hi == 0, fresh_window(tile_of(it_hi)));
+    o_phase(it_hi % NST);
+  }
+  // The rest of the work-group's steps: loads and synchronisation only.
+  for (int it = it_hi + 1; it < n_steps; ++it) {
+    const int st = (it + PF) % NST;
+    load_tile(tile_or_none(tile_of(it + PF)), st, st);
+    sync();
+  }
   // Zero-fill loads issued past the last tile may still be writing LDS.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
