@@ -41,8 +41,7 @@
 //     the wave issues it;
 //   * tiles are loaded PF tiles ahead of the math into free LDS stages (PF+1
 //     for K, PF+2 for V because the PV products lag one tile), which hides
-//     the L2/HBM latency behind several tiles of math; one barrier per tile
-//     (none when each key group of a key-split instance is one wave);
+//     the L2/HBM latency behind several tiles of math; one barrier per tile;
 //   * causal and sliding-window masks skip whole tiles: the work-group visits
 //     only key tiles that intersect its rows' visible band, and the
 //     elementwise mask (scores set to -inf) runs only on tiles that straddle
@@ -702,9 +701,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   //
   // Every wave of a key group runs every tile of that group (the loads are
   // shared within the group; every wave takes the same number of steps).
-  // When a key group is a single wave (NR = 1), no other wave reads or
-  // writes its stages, so its own load-counter wait is all a step needs and
-  // the waves run without a barrier until the merge.  A wave masks a tile
+  // A wave masks a tile
   // elementwise when the tile straddles an edge of its rows' band or lies
   // outside it; a tile outside the band is simply fully masked (weights 0,
   // factor 1).
@@ -740,7 +737,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   if (NK == 1 && MASK != kMaskNone) it_hi = min(it_hi, min(wr1, S - 1) / BC - kt_begin);
   auto sync = [&]() __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
-    if constexpr (NR > 1) __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_barrier();
   };
   auto step = [&](auto phase_c, int it) __attribute__((always_inline)) {
     const int kt = tile_of(it);
