@@ -21,6 +21,8 @@
 // for every compute unit seen in both, the mean shader clock over that
 // stretch:
 //   (cycles_after - cycles_before) / (real_after - real_before) * real_rate.
+// The cycle counter advances only while the compute unit is active, so the
+// stretch must be continuous work (idle gaps read as a lower clock).
 // n = 1024 work-groups visit almost every one of the 256 compute units.
 //
 // fa_mfma_ceiling measures what the matrix cores sustain on this part when
