@@ -221,6 +221,37 @@ def test_ragged_lengths(S, mask, window):
     _check_full(q, k, v, mask, window, 1.0 / math.sqrt(128), "bf16", f"ragged S={S} {mask}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d,mask,window", [(64, "none", None), (64, "causal", None),
+                                           (64, "window", 256), (64, "window", 333),
+                                           (128, "window", 512), (128, "causal", None)])
+def test_key_split_long_bands(dtype, d, mask, window):
+    # B = 1, H = 2: the plain grid is far below one work-group per compute
+    # unit, so the keys of every work-group are split over key groups (4 at
+    # d = 64, 2 at d = 128) with many tiles per group; windows a multiple of
+    # the 32-key tile and not, and a ragged S.
+    S = 2900
+    name, _ = fa.fa_query_fwd(1, 2, 2, S, d, fa.DTYPES[dtype], fa.MASKS[mask], window or 0)
+    assert name.endswith(f"keysplit{4 if d == 64 else 2}>"), name
+    q, k, v = make_inputs(1, 2, S, d, dtype, seed=d * 11 + (window or 0))
+    _check_full(q, k, v, mask, window, 1.0 / math.sqrt(d), dtype,
+                f"key split {dtype} d={d} {mask} W={window} S={S}")
+
+
+@pytest.mark.parametrize("d,mask,window", [(128, "causal", None), (128, "window", 100),
+                                           (64, "causal", None), (64, "window", 65)])
+def test_plain_grid_last_rows_past_the_sequence(d, mask, window):
+    # 64 heads of S = 900: at least 256 work-groups, so no key split, and
+    # the last work-group of each head (rows 768..1023) has waves whose rows
+    # all lie past S and waves that straddle it.
+    name, grid = fa.fa_query_fwd(1, 64, 64, 900, d, fa.DTYPES["bf16"], fa.MASKS[mask],
+                                 window or 0)
+    assert "keysplit" not in name and "br256" in name and grid == 256, (name, grid)
+    q, k, v = make_inputs(1, 64, 900, d, "bf16", seed=900 + d)
+    _check_full(q, k, v, mask, window, 1.0 / math.sqrt(d), "bf16",
+                f"plain grid d={d} {mask} W={window} S=900 H=64")
+
+
 def test_many_heads_small_sequence():
     q, k, v = make_inputs(3, 40, 65, 64, "bf16", seed=5)
     _check_full(q, k, v, "causal", None, 0.125, "bf16", "B=3 H=40 S=65")
