@@ -296,6 +296,19 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
                   8 * (lane & 1);
     }
   }
+  // The V stages follow the K stages in LDS.  With several key groups or
+  // d = 256 they reach past 64 KB, beyond the 16-bit offset of an LDS
+  // instruction: the bases then carry the V array's LDS address themselves
+  // (opaque to the compiler, which would otherwise fold it back into the
+  // constant and add it with a vector instruction before each read), so
+  // that the stage and step stay in the offset field.
+  constexpr bool V_FAR = sizeof(k_lds) + NST * STAGE_BYTES > 65536;
+  uint32_t v_at[NVB];
+#pragma unroll
+  for (int j = 0; j < NVB; ++j) {
+    v_at[j] = (V_FAR ? (uint32_t)(uintptr_t)&v_lds[0][0][0] : 0u) + (uint32_t)v_base[j];
+    if (V_FAR) asm volatile("" : "+v"(v_at[j]));
+  }
   auto v_off = [](int kk, int db) constexpr { return 16 * kk * (D * 2) + 64 * (db & ~3); };
 
   // K operand of score step st = (ks, kb): 16 bytes per lane.
@@ -303,14 +316,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     const int ks = st / NKB, kb = st % NKB;
     return *(const u32x4 *)(kl + k_base[ks % KSW] + kb * (32 * D * 2) + 16 * 2 * KSW * (ks / KSW));
   };
-  // V^T operand of product step st = (kk, db): two transposing reads.
-  auto read_v = [&](const char *vl, int st) __attribute__((always_inline)) {
+  // V^T operand of product step st = (kk, db) from the V stage at byte
+  // offset vs of the V array: two transposing reads.
+  auto read_v = [&](uint32_t vs, int st) __attribute__((always_inline)) {
     const int kk = st / NDB, db = st % NDB;
     u32x4 op;
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2) {
+      const uint32_t o = v_at[2 * (db & 3) + i2] + vs + v_off(kk, db);
       const u32x2 v2 = lds_read_tr16(
-          (const FA_LDS void *)(vl + v_base[2 * (db & 3) + i2] + v_off(kk, db)));
+          V_FAR ? (const FA_LDS void *)(uintptr_t)o
+                : (const FA_LDS void *)((const char *)&v_lds[0][0][0] + o));
       op[2 * i2] = v2[0];
       op[2 * i2 + 1] = v2[1];
     }
@@ -318,7 +334,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   };
   // O_h^T += V^T P_h^T for every half, without interleaved work (last tile).
   auto o_phase = [&](int vst) __attribute__((always_inline)) {
-    const char *vl = (const char *)&v_lds[0][vst][0];
+    const uint32_t vl = (uint32_t)vst * STAGE_BYTES;
 #pragma unroll
     for (int st = 0; st < NPS * NDB; ++st) {
       const u32x4 op = read_v(vl, st);
@@ -352,8 +368,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
           lower = k0 <= r1 - a.window;
         }
       }
-      const int row = r0 + lq;
-      auto key_of = [&](int kb, int r) { return k0 + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3); };
+      // Score (kb, r) of this lane holds key k0 + 4 * lg + off(kb, r) of
+      // row r0 + lq; each edge test compares the compile-time offset with
+      // one per-lane bound (no index arithmetic per score).
+      const int kbase = k0 + 4 * lg, row = r0 + lq;
+      auto off = [](int kb, int r) constexpr { return 32 * kb + 8 * (r >> 2) + (r & 3); };
       if (none_visible) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -361,26 +380,29 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
           for (int r = 0; r < 16; ++r) sacc[h][kb][r] = -INFINITY;
         continue;
       }
-      if (upper) {
+      if (upper) {  // key > row
+        const int t = row - kbase;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (key_of(kb, r) > row) sacc[h][kb][r] = -INFINITY;
+            if (off(kb, r) > t) sacc[h][kb][r] = -INFINITY;
       }
-      if (MASK == kMaskWindow && lower) {
+      if (MASK == kMaskWindow && lower) {  // key <= row - window
+        const int t = row - a.window - kbase;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (key_of(kb, r) <= row - a.window) sacc[h][kb][r] = -INFINITY;
+            if (off(kb, r) <= t) sacc[h][kb][r] = -INFINITY;
       }
-      if (MASK == kMaskNone && tail) {
+      if (MASK == kMaskNone && tail) {  // key >= S
+        const int t = S - kbase;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (key_of(kb, r) >= S) sacc[h][kb][r] = -INFINITY;
+            if (off(kb, r) >= t) sacc[h][kb][r] = -INFINITY;
       }
     }
   };
@@ -569,7 +591,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
     constexpr int P = decltype(phase_c)::value;
     constexpr int kst = P, vprev = (P + NST - 1) % NST, lks = (P + PF) % NST, lvs = lks;
     const char *kl = (const char *)&k_lds[0][kst][0];
-    const char *vl = (const char *)&v_lds[0][vprev][0];
+    constexpr uint32_t vl = vprev * STAGE_BYTES;
     const int lk0 = lkt * BC;
     // Direct load d of tile t+PF (K and V alternate), issued after MFMA 2d+1
     // of phase A (placements over both phases, or all at once, measured no
