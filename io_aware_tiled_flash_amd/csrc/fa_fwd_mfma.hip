@@ -197,13 +197,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   for (int h = 0; h < NH; ++h)
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      qreg[h][ks] = load16(rq, (uint32_t)((wr0 + 32 * h + lq) * D + 16 * ks + 8 * lg) * 2u) ^ qflip;
-  // Q never meets the vector ALU again: keep it in accumulation registers
-  // (MFMA reads its A/B operands from AGPRs too), leaving VGPRs to the softmax.
-#pragma unroll
-  for (int h = 0; h < NH; ++h)
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qreg[h][ks]));
+      qreg[h][ks] = load16(rq, (uint32_t)((wr0 + 32 * h + lq) * D + 16 * ks + 8 * lg) * 2u);
 
   // Key tiles this work-group visits.
   const int ntk = (S + BC - 1) / BC;
@@ -700,6 +694,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   auto tile_or_none = [&](int kt) { return kt < kt_end ? kt : kt_none; };
 #pragma unroll
   for (int i = 0; i < PF; ++i) load_tile(tile_or_none(tile_of(i)), i, i);
+  __builtin_amdgcn_sched_barrier(0);  // nothing that waits for Q before these loads
   // Wait for the first tile only (and the zero fill); the later prefetches
   // stay in flight.
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS_PER_TILE * (PF - 1)) : "memory");
@@ -712,6 +707,18 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   // a loop, makes it wait for lgkmcnt(0), which also drains the LDS operand
   // reads that run ahead of the MFMAs.
   asm volatile("" ::"s"(rk), "s"(rv), "s"(a.o), "s"(a.lse));
+  // The sign flip, then Q into accumulation registers: Q never meets the
+  // vector ALU again, and MFMA reads its A/B operands from AGPRs too, which
+  // leaves the VGPRs to the softmax.  Both wait for the Q loads, so they come
+  // after the first tiles' loads are issued (the fence above keeps them
+  // there): Q and those tiles are then fetched in one round trip.
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qreg[h][ks] ^= qflip;
+      asm volatile("" : "+a"(qreg[h][ks]));
+    }
 
   // The work-group's steps run in groups of NST, each copy of the tile with
   // its own compile-time stage phase; the loop leaves at the first step past
