@@ -168,10 +168,21 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(FwdArgs a) {
   const int BH = a.B * a.H;
   const int nq = (S + BR - 1) / BR;
 
-  const HeadPair hp = head_of_slot(blockIdx.x % BH, a.B, a.H, a.Hkv);
+  // Work-group b runs on XCD b % 8.  Masked launches take one query tile of
+  // each head at a time, heaviest first (their tiles differ in work).
+  // Unmasked ones, whose tiles are all alike, run every query tile of one
+  // head in a row on its XCD, so the XCD's resident work-groups share few
+  // heads' K and V in its L2.
+  int slot = blockIdx.x % BH, qt = blockIdx.x / BH;
+  if (MASK != kMaskNone) {
+    qt = nq - 1 - qt;
+  } else if (BH % 8 == 0) {
+    const int xcd = blockIdx.x % 8, l = blockIdx.x / 8;
+    slot = (l / nq) * 8 + xcd;
+    qt = l % nq;
+  }
+  const HeadPair hp = head_of_slot(slot, a.B, a.H, a.Hkv);
   const int bh = hp.q;
-  int qt = blockIdx.x / BH;
-  if (MASK != kMaskNone) qt = nq - 1 - qt;  // heaviest query tiles first
   const int q0 = qt * BR;
 
   const size_t head_off = (size_t)bh * (size_t)S * D;     // q, o (elements)
