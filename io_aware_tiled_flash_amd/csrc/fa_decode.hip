@@ -286,8 +286,19 @@ __global__ __launch_bounds__(kThreads) void fa_decode_merge_kernel(DecodeArgs a)
   if (ns_b == 1) return;  // written directly by the split kernel
   const float *ls = a.ws_lse + (size_t)row * a.n_splits;
   const float *os = a.ws_o + (size_t)row * a.n_splits * D;
-  float mx = -INFINITY;
-  for (int s = lane; s < ns_b; s += 64) mx = fmaxf(mx, ls[s]);
+  // The first U splits' partial rows are loaded together with the
+  // logsumexps (past the last split: the last one again, a valid address,
+  // later given weight 0), so the common case costs one round trip.
+  float v0[U][CPL];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int s = min(u, ns_b - 1);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v0[u][c] = os[(size_t)s * D + lane + 64 * c];
+  }
+  const float ls_lane = lane < ns_b ? ls[lane] : -INFINITY;  // split `lane`'s logsumexp
+  float mx = ls_lane;
+  for (int s = lane + 64; s < ns_b; s += 64) mx = fmaxf(mx, ls[s]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   uint16_t *orow = (uint16_t *)a.o + (size_t)row * D;
@@ -298,8 +309,8 @@ __global__ __launch_bounds__(kThreads) void fa_decode_merge_kernel(DecodeArgs a)
     return;
   }
   constexpr float kLog2e = 1.4426950408889634f;
-  float sum = 0.f;
-  for (int s = lane; s < ns_b; s += 64) sum += __builtin_amdgcn_exp2f((ls[s] - mx) * kLog2e);
+  float sum = lane < ns_b ? __builtin_amdgcn_exp2f((ls_lane - mx) * kLog2e) : 0.f;
+  for (int s = lane + 64; s < ns_b; s += 64) sum += __builtin_amdgcn_exp2f((ls[s] - mx) * kLog2e);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
   const float lse = mx + __builtin_amdgcn_logf(sum) * 0.69314718055994531f;
@@ -310,11 +321,13 @@ __global__ __launch_bounds__(kThreads) void fa_decode_merge_kernel(DecodeArgs a)
     float w[U], v[U][CPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      // past the last split: re-read the last one (a valid address) with weight 0
       const int s = min(s0 + u, ns_b - 1);
-      w[u] = s0 + u < ns_b ? __builtin_amdgcn_exp2f((ls[s] - lse) * kLog2e) : 0.f;
+      // split s's logsumexp: from lane s for the first 64, else from memory
+      const float lss = s < 64 ? __shfl(ls_lane, s, 64) : ls[s];
+      w[u] = s0 + u < ns_b ? __builtin_amdgcn_exp2f((lss - lse) * kLog2e) : 0.f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) v[u][c] = os[(size_t)s * D + lane + 64 * c];
+      for (int c = 0; c < CPL; ++c)
+        v[u][c] = s0 == 0 ? v0[u][c] : os[(size_t)s * D + lane + 64 * c];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
