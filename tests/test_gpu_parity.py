@@ -252,6 +252,22 @@ def test_plain_grid_last_rows_past_the_sequence(d, mask, window):
                 f"plain grid d={d} {mask} W={window} S=900 H=64")
 
 
+@pytest.mark.parametrize("dtype,d,B,H,Hkv,S", [("bf16", 128, 2, 16, 16, 2100),
+                                                 ("bf16", 128, 2, 16, 4, 2100),
+                                                 ("f16", 256, 4, 8, 8, 1000),
+                                                 ("bf16", 64, 1, 56, 56, 1100),
+                                                 ("bf16", 128, 1, 36, 36, 2100)])
+def test_unmasked_head_order(dtype, d, B, H, Hkv, S):
+    # Unmasked launches of at least 256 work-groups (no key split) with several
+    # query tiles per head: B * H a multiple of 8 takes the order that runs a
+    # head's query tiles in a row on one XCD; B * H = 36 keeps the plain order.
+    name, grid = fa.fa_query_fwd(B, H, Hkv, S, d, fa.DTYPES[dtype], fa.MASKS["none"], 0)
+    assert "keysplit" not in name and grid >= 256, (name, grid)
+    q, k, v = make_inputs(B, H, S, d, dtype, seed=S + H + d, Hkv=Hkv)
+    _check_full(q, k, v, "none", None, 1.0 / math.sqrt(d), dtype,
+                f"unmasked order {dtype} d={d} B={B} H={H} Hkv={Hkv} S={S}")
+
+
 def test_many_heads_small_sequence():
     q, k, v = make_inputs(3, 40, 65, 64, "bf16", seed=5)
     _check_full(q, k, v, "causal", None, 0.125, "bf16", "B=3 H=40 S=65")
