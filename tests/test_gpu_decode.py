@@ -110,6 +110,17 @@ def test_decode_cases(dtype, d, B, H, Hkv, n_q, bs, ctx):
     _check(B, H, Hkv, n_q, d, dtype, bs, ctx)
 
 
+@pytest.mark.parametrize("H", [8, 16])  # 4 rows per key/value head (vector kernel), 8 (matrix core)
+def test_decode_more_than_64_splits(H):
+    # A 70,000-token request in 1,024-token splits: the merge takes the
+    # logsumexps of splits 64 and up from memory rather than from the wave's
+    # lanes, and combines its partial rows in several groups.
+    ws = fa.fa_decode_workspace_size(1, H, 2, 1, 128, 1, 16, 4400, 70000, 2)
+    n_splits = ws // (H * 129 * 4)
+    assert n_splits > 64, n_splits
+    _check(1, H, 2, 1, 128, "bf16", 16, (70000,))
+
+
 @pytest.mark.parametrize("ctx", [(5000,), (4096, 1, 12000), (9000, 0, 4097)])
 def test_decode_long_contexts_are_split_and_merged(ctx):
     B = len(ctx)
