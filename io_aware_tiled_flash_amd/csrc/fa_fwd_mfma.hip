@@ -950,8 +950,13 @@ template <class Ty, int D, int MASK, int NK>
 struct Instance {
   // Key splits (d <= 128): 8 waves of 32 rows, two per SIMD (169 registers
   // at d = 64, about 200 at d = 128), so that a step's softmax work is split
-  // over twice the waves; everything else: 4 waves, one per SIMD.
-  static constexpr int NW = (D <= 128 && NK > 1) ? 8 : 4;
+  // over twice the waves.  The d = 128 sliding window: 2 waves of 64 rows,
+  // two work-groups per compute unit, so that a barrier couples only the two
+  // waves of a 128-row band (their band edges, and so their masked tiles,
+  // fall on different steps) and a work-group's band holds 2 tiles more than
+  // a wave's instead of 6.  Everything else: 4 waves, one per SIMD.
+  static constexpr int NW = (D <= 128 && NK > 1) ? 8
+                            : (D == 128 && MASK == kMaskWindow) ? 2 : 4;
   static constexpr int BC = NK > 1 ? 32 : D == 64 ? 64 : 32;  // keys per tile
   static constexpr int NH = (D <= 128 && NK > 1) ? 1 : D <= 128 ? 2 : 1;
   static constexpr int PF = 2;

@@ -73,6 +73,10 @@ def test_query_fwd_names_the_instance_for_the_sizes():
     # large grids: the plain instance, one work-group per 256 query rows
     name, grid = fa.fa_query_fwd(1, 32, 32, 8192, 128, fa.DTYPES["bf16"], fa.MASKS["causal"])
     assert name == fa.fa_query(128, fa.DTYPES["bf16"], fa.MASKS["causal"]) and grid == 32 * 32
+    # the d = 128 sliding window: 128-row work-groups of two waves
+    name, grid = fa.fa_query_fwd(1, 16, 16, 18432, 128, fa.DTYPES["bf16"], fa.MASKS["window"],
+                                 4096)
+    assert "br128" in name and "keysplit" not in name and grid == 144 * 16
     # fewer work-groups than compute units: keys split over the waves
     name, grid = fa.fa_query_fwd(2, 8, 8, 1024, 64, fa.DTYPES["bf16"], fa.MASKS["causal"])
     assert "keysplit4" in name and "br64" in name and grid == 16 * 16

@@ -242,11 +242,14 @@ def test_key_split_long_bands(dtype, d, mask, window):
                                            (64, "causal", None), (64, "window", 65)])
 def test_plain_grid_last_rows_past_the_sequence(d, mask, window):
     # 64 heads of S = 900: at least 256 work-groups, so no key split, and
-    # the last work-group of each head (rows 768..1023) has waves whose rows
-    # all lie past S and waves that straddle it.
+    # the last work-group of each head (rows 768..1023, or 896..1023 for the
+    # 128-row d = 128 window instance) has waves whose rows all lie past S
+    # and a wave that straddles it.
     name, grid = fa.fa_query_fwd(1, 64, 64, 900, d, fa.DTYPES["bf16"], fa.MASKS[mask],
                                  window or 0)
-    assert "keysplit" not in name and "br256" in name and grid == 256, (name, grid)
+    br = 128 if (d, mask) == (128, "window") else 256
+    assert "keysplit" not in name and f"br{br}" in name and grid == 64 * (1024 // br), \
+        (name, grid)
     q, k, v = make_inputs(1, 64, 900, d, "bf16", seed=900 + d)
     _check_full(q, k, v, mask, window, 1.0 / math.sqrt(d), "bf16",
                 f"plain grid d={d} {mask} W={window} S=900 H=64")
