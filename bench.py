@@ -543,8 +543,11 @@ def main() -> int:
                   f"% of MFMA {w.dtype} peak")
         kernel = "fa_bwd: " + ", ".join(BWD_KERNELS)
     else:
+        # fp32 inputs run on the vector ALUs (no down-conversion): their peak
+        # is the fp32 vector rate, and the bound is the ALUs, not the MFMA
+        unit_name = "fp32 vector" if w.dtype == "f32" else f"MFMA {w.dtype}"
         metric = METRIC if w.name == HEADLINE else (
-            f"attention fwd TFLOP/s on {w.name}; % of MFMA {w.dtype} peak")
+            f"attention fwd TFLOP/s on {w.name}; % of {unit_name} peak")
         kernel = fa.fa_query_fwd(w.B, w.H, w.kv_heads, w.S, w.d, fa.DTYPES[w.dtype],
                                  fa.MASKS[w.mask], int(w.window or 0))[0]
     result = {
@@ -565,7 +568,8 @@ def main() -> int:
                    "mask": w.mask, "window": w.window or None, "input_dtype": w.dtype,
                    "pass": args.pass_, "kernel": kernel},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+        "roofline": {"bound": "alu" if w.dtype == "f32" else "mfma",
+                     "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": traffic},
         "step_ms": stats,
