@@ -376,6 +376,23 @@ def test_deterministic_repeat():
         assert torch.equal(o, runs[0][0]) and torch.equal(lse, runs[0][1])
 
 
+@pytest.mark.parametrize("dtype,d,B,H,Hkv,S,mask,window", [
+    ("bf16", 128, 1, 32, 32, 2048, "causal", None),   # plain 256-row instance
+    ("bf16", 128, 1, 16, 16, 3000, "window", 700),    # two-wave window instance
+    ("f16", 256, 2, 16, 16, 1024, "none", None),      # d = 256, head-grouped order
+    ("bf16", 128, 2, 16, 4, 1500, "none", None),      # grouped key/value heads
+    ("f32", 128, 1, 8, 8, 700, "causal", None),       # fp32 quad-per-row kernel
+])
+def test_deterministic_repeat_instances(dtype, d, B, H, Hkv, S, mask, window):
+    # Run-to-run bit identity of every instance family: no atomics, fixed
+    # reduction orders.
+    q, k, v = make_inputs(B, H, S, d, dtype, seed=S + d, Hkv=Hkv)
+    _say(f"determinism {dtype} d={d} {mask} H={H} Hkv={Hkv} S={S}")
+    runs = [_run(q, k, v, mask, window, 1.0 / math.sqrt(d)) for _ in range(3)]
+    for o, lse in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(lse, runs[0][1])
+
+
 def test_outputs_do_not_touch_neighbours():
     """The kernel writes exactly o and lse: guard bands around them stay intact."""
     dev = torch.device("cuda:0")
