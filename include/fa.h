@@ -214,7 +214,8 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
  *              (host value; it sizes the split and the workspace).  Longer
  *              contexts are cut to max_ctx tokens.
  * block_size : a power of two, 1 .. 1024.
- * Supported: FA_F16 / FA_BF16 with d in {64, 128}.
+ * Supported: FA_F16 / FA_BF16 with d in {64, 128, 256} (at 256 every row
+ *            count runs on the vector kernel).
  *
  * Ownership, stream order and determinism as for fa_fwd (one or two launches).
  * Errors, checked on the host before any launch:
@@ -225,7 +226,7 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
  *                   dividing H; unknown dtype; a scale rejected as by fa_fwd; workspace
  *                   smaller than required; o, lse or workspace overlapping an
  *                   input or each other; sizes beyond the kernels' index range.
- *   FA_EUNSUPPORTED FA_F32, d outside {64, 128}, or a block_size that is not a
+ *   FA_EUNSUPPORTED FA_F32, d outside {64, 128, 256}, or a block_size that is not a
  *                   power of two up to 1024.
  *   FA_EHIP         a launch failed.
  * Values inside block_table and ctx_lens are device data and are never

@@ -289,7 +289,7 @@ fa_status decode_sizes(int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t d
   if (max_ctx < cap) cap = max_ctx;
   if (dtype == FA_F32 || !fa::decode_plan((int)d, B, H, Hkv, n_q, cap, plan))
     return fail(FA_EUNSUPPORTED, "no decode kernel for dtype=%s d=%lld (supported: bf16/f16 "
-                "with d in {64,128})", dtype_name(dtype), (long long)d);
+                "with d in {64,128,256})", dtype_name(dtype), (long long)d);
   if (plan->grid > INT32_MAX) return fail(FA_EINVAL, "grid too large");
   *bs_shift = sh;
   *ctx_cap = cap;

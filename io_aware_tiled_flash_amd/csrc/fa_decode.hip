@@ -62,9 +62,9 @@ template <> struct Dot<TF16> {
   }
 };
 
-// Sum over the LPT lanes of a token group (a DPP row of 16 lanes or half of
-// one); every lane of the group ends with the same bits (each step adds the
-// same two partial sums, in either order).
+// Sum over the LPT lanes of a token group (half a DPP row of 16 lanes, a
+// row, or two rows); every lane of the group ends with the same bits (each
+// step adds the same two partial sums, in either order).
 template <int LPT>
 __device__ inline float group_sum(float x) {
   auto add = [](float v, auto ctrl) __attribute__((always_inline)) {
@@ -75,7 +75,8 @@ __device__ inline float group_sum(float x) {
   x = add(x, std::integral_constant<int, 0xb1>{});   // quad_perm [1,0,3,2]
   x = add(x, std::integral_constant<int, 0x4e>{});   // quad_perm [2,3,0,1]
   x = add(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
-  if (LPT == 16) x = add(x, std::integral_constant<int, 0x140>{});  // row_mirror
+  if (LPT >= 16) x = add(x, std::integral_constant<int, 0x140>{});  // row_mirror
+  if (LPT == 32) x += __shfl_xor(x, 16, 64);                        // the other row
   return x;
 }
 
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeArgs a)
   constexpr int LPT = D / 8;         // lanes per token
   constexpr int TPW = 64 / LPT;      // tokens per wave per step
   constexpr int TPS = 4 * TPW;       // tokens per work-group per step
-  static_assert(LPT == 8 || LPT == 16, "d must be 64 or 128");
+  static_assert(LPT == 8 || LPT == 16 || LPT == 32, "d must be 64, 128 or 256");
   __shared__ int tab[kMaxTable];
   __shared__ float red_m[4][R], red_l[4][R];
   __shared__ float red_o[4][R][D];
@@ -664,7 +665,9 @@ bool decode_by_rows(const DecodeArgs *a, const DecodePlan *p, hipStream_t s, boo
     case 1: return run_decode<Ty, D, 1>(a, p, s, launch, info, err);
     case 2: return run_decode<Ty, D, 2>(a, p, s, launch, info, err);
     case 4: return run_decode<Ty, D, 4>(a, p, s, launch, info, err);
-    case 16: return run_decode_m16<Ty, D>(a, p, s, launch, info, err);
+    case 16:
+      if constexpr (D <= 128) return run_decode_m16<Ty, D>(a, p, s, launch, info, err);
+      return false;
   }
   return false;
 }
@@ -675,6 +678,7 @@ bool decode_by_dim(int d, const DecodeArgs *a, const DecodePlan *p, hipStream_t 
   switch (d) {
     case 64: return decode_by_rows<Ty, 64>(a, p, s, launch, info, err);
     case 128: return decode_by_rows<Ty, 128>(a, p, s, launch, info, err);
+    case 256: return decode_by_rows<Ty, 256>(a, p, s, launch, info, err);
   }
   return false;
 }
@@ -683,7 +687,7 @@ bool decode_by_dim(int d, const DecodeArgs *a, const DecodePlan *p, hipStream_t 
 
 bool decode_plan(int d, int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t ctx_cap,
                  DecodePlan *p) {
-  if (d != 64 && d != 128) return false;
+  if (d != 64 && d != 128 && d != 256) return false;
   const int64_t rows_total = (H / Hkv) * n_q;
   // A key/value head serving many query rows goes to the matrix-core kernel
   // (16 rows per work-group); up to kMfmaRows - 1 rows stay on the vector
@@ -693,7 +697,11 @@ bool decode_plan(int d, int64_t B, int64_t H, int64_t Hkv, int64_t n_q, int64_t 
   // rows per work-group: more rows slices (whose repeated cache reads hit
   // the shared L2) measured faster than 8-row work-groups, whose registers
   // cut the waves per SIMD from 5 to 3.
-  p->rows = rows_total <= 1 ? 1 : rows_total <= 2 ? 2 : rows_total < kMfmaRows ? 4 : 16;
+  // At d = 256 every row count takes the vector kernel (in 4-row slices):
+  // the matrix-core kernel's two register sets of 16 K and V rows would not
+  // fit beside its accumulators.
+  p->rows = rows_total <= 1 ? 1 : rows_total <= 2 ? 2
+          : (rows_total < kMfmaRows || d == 256) ? 4 : 16;
   p->row_slices = (int)((rows_total + p->rows - 1) / p->rows);
   // Enough work-groups to fill the chip several times over: split each
   // context when requests x key/value heads x row slices alone are too few,

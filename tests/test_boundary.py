@@ -266,7 +266,7 @@ def test_decode_invalid_arguments_are_rejected_before_any_launch(kw, needle):
     assert needle in fa.fa_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(dtype=0), dict(d=96), dict(d=256), dict(block_size=24),
+@pytest.mark.parametrize("kw", [dict(dtype=0), dict(d=96), dict(d=512), dict(block_size=24),
                                 dict(block_size=2048)])
 def test_decode_unsupported_configuration_is_an_error(kw):
     assert _call_decode(**kw) == fa.FA_EUNSUPPORTED

@@ -105,6 +105,22 @@ CASES = [
 ]
 
 
+D256_CASES = [
+    # dtype, d, B, H, Hkv, n_q, bs, ctx  (d = 256: 32 lanes per token)
+    ("bf16", 256, 3, 4, 4, 1, 16, (1, 37, 700)),      # one row per key/value head
+    ("f16", 256, 2, 4, 2, 1, 16, (5, 300)),           # two rows
+    ("bf16", 256, 2, 8, 2, 1, 16, (64, 1000)),        # four rows
+    ("f16", 256, 1, 16, 2, 2, 16, (900,)),            # 16 rows: four 4-row slices
+    ("bf16", 256, 2, 8, 2, 1, 16, (5000, 33)),        # split context and merge
+    ("bf16", 256, 1, 4, 1, 3, 8, (2500,)),            # 12 rows, split, n_q = 3
+]
+
+
+@pytest.mark.parametrize("dtype,d,B,H,Hkv,n_q,bs,ctx", D256_CASES)
+def test_decode_head_dim_256(dtype, d, B, H, Hkv, n_q, bs, ctx):
+    _check(B, H, Hkv, n_q, d, dtype, bs, ctx)
+
+
 @pytest.mark.parametrize("dtype,d,B,H,Hkv,n_q,bs,ctx", CASES)
 def test_decode_cases(dtype, d, B, H, Hkv, n_q, bs, ctx):
     _check(B, H, Hkv, n_q, d, dtype, bs, ctx)
