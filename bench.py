@@ -82,7 +82,8 @@ def measured_traffic(workload: str, sources=FWD_SOURCES):
         if ":" in line and not line.startswith("#"):
             key, _, val = line.partition(":")
             vals[key.strip()] = val.strip()
-    if vals.get("kernel_source_digest") != kernel_source_digest(sources):
+    # (the digest line may name its sources after the digest)
+    if (vals.get("kernel_source_digest") or "").split()[:1] != [kernel_source_digest(sources)]:
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))

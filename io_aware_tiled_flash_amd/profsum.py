@@ -132,7 +132,8 @@ def cmd_traffic(a) -> list[str]:
             f"hbm_read_bytes_per_launch: {rd:.0f}",
             f"hbm_write_bytes_per_launch: {wr:.0f}",
             f"hbm_bytes_per_launch: {rd + wr:.0f}",
-            f"kernel_source_digest: {bench.kernel_source_digest(tuple(a.sources))}"]
+            f"kernel_source_digest: {bench.kernel_source_digest(tuple(a.sources))}"
+            f"  ({' '.join(a.sources)})"]
     return out
 
 
@@ -209,7 +210,8 @@ def cmd_sq(a) -> list[str]:
     if "SQ_LDS_BANK_CONFLICT" in vals and "SQ_INSTS_LDS" in vals:
         out.append(f"  lds_bank_conflict_cycles per LDS instruction: "
                    f"{vals['SQ_LDS_BANK_CONFLICT'] / max(vals['SQ_INSTS_LDS'], 1):.4f}")
-    out.append(f"kernel_source_digest: {bench.kernel_source_digest(tuple(a.sources))}")
+    out.append(f"kernel_source_digest: {bench.kernel_source_digest(tuple(a.sources))}"
+               f"  ({' '.join(a.sources)})")
     return out
 
 
