@@ -393,19 +393,27 @@ def test_deterministic_repeat_instances(dtype, d, B, H, Hkv, S, mask, window):
         assert torch.equal(o, runs[0][0]) and torch.equal(lse, runs[0][1])
 
 
-def test_outputs_do_not_touch_neighbours():
+@pytest.mark.parametrize("dtype,d,H,S,mask,window", [
+    ("bf16", 64, 2, 130, "causal", None),     # key-split instance
+    ("bf16", 128, 128, 300, "window", 70),    # plain two-wave window instance
+    ("f16", 256, 64, 200, "none", None),      # d = 256, head-grouped order
+    ("f32", 128, 4, 77, "window", 20),        # fp32 quad-per-row kernel
+])
+def test_outputs_do_not_touch_neighbours(dtype, d, H, S, mask, window):
     """The kernel writes exactly o and lse: guard bands around them stay intact."""
     dev = torch.device("cuda:0")
-    q, k, v = (t.to(dev) for t in make_inputs(1, 2, 130, 64, "bf16", seed=16))
-    big = torch.full((3 * q.numel(),), 7.0, dtype=torch.bfloat16, device=dev)
-    out = big[q.numel():2 * q.numel()].view_as(q)
-    lbig = torch.full((3 * 260,), 9.0, dtype=torch.float32, device=dev)
-    lse = lbig[260:520].view(1, 2, 130)
-    _say("guard bands")
-    fa.forward(q, k, v, mask="causal", out=out, lse=lse)
+    q, k, v = (t.to(dev) for t in make_inputs(1, H, S, d, dtype, seed=16))
+    n, nl = q.numel(), H * S
+    big = torch.full((3 * n,), 7.0, dtype=q.dtype, device=dev)
+    out = big[n:2 * n].view_as(q)
+    lbig = torch.full((3 * nl,), 9.0, dtype=torch.float32, device=dev)
+    lse = lbig[nl:2 * nl].view(1, H, S)
+    _say(f"guard bands {dtype} d={d} H={H} S={S} {mask}")
+    fa.forward(q, k, v, mask=mask, window=window, out=out, lse=lse)
     torch.cuda.synchronize()
-    assert bool((big[:q.numel()] == 7.0).all()) and bool((big[2 * q.numel():] == 7.0).all())
-    assert bool((lbig[:260] == 9.0).all()) and bool((lbig[520:] == 9.0).all())
+    assert bool((big[:n] == 7.0).all()) and bool((big[2 * n:] == 7.0).all())
+    assert bool((lbig[:nl] == 9.0).all()) and bool((lbig[2 * nl:] == 9.0).all())
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
 
 
 def test_forward_refuses_host_outputs(monkeypatch):
