@@ -243,12 +243,15 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     return e;
   };
   auto fix_mask = [&](int row0, u32x4 (&pk)[2]) __attribute__((always_inline)) {
-    const int key = kw0 + lq;
+    // row = row0 + 4*lg + off(r): key <= row is off(r) >= t, and under a
+    // window key > row - window is off(r) < t + window (one per-lane bound,
+    // compile-time offsets)
+    const int t = kw0 + lq - row0 - 4 * lg;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = row0 + 8 * (r >> 2) + 4 * lg + (r & 3);
-      bool vis = key <= row;
-      if (MASK == kMaskWindow) vis = vis && key > row - a.window;
+      const int off = 8 * (r >> 2) + (r & 3);
+      bool vis = off >= t;
+      if (MASK == kMaskWindow) vis = vis && off < t + a.window;
       if (!vis) pw[r] = 0.f;
     }
 #pragma unroll
@@ -524,12 +527,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
     return false;
   };
   auto fix_mask = [&](int u) __attribute__((always_inline)) {
-    const int k0 = (kt_begin + u) * BC;
+    // key = k0 + 4*lg + off(r): key <= row is off(r) <= t, and under a
+    // window key > row - window is off(r) > t - window
+    const int t = row - (kt_begin + u) * BC - 4 * lg;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * lg + (r & 3);
-      bool vis = key <= row;
-      if (MASK == kMaskWindow) vis = vis && key > row - a.window;
+      const int off = 8 * (r >> 2) + (r & 3);
+      bool vis = off <= t;
+      if (MASK == kMaskWindow) vis = vis && off > t - a.window;
       if (!vis) pw[r] = 0.f;
     }
   };
