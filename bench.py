@@ -272,6 +272,49 @@ def time_steps(step, stream, steps: int, warmup: int, settle_s: float, clock=Non
     return mean_ms, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)], settle
 
 
+def time_graph(run, stream, steps: int, warmup: int, settle_s: float, clock=None):
+    """Graph mode (forward only): settle and warm up with ordinary launches,
+    then capture `steps` calls of run(stream) once into a HIP graph on a side
+    stream and time one replay of it on `stream` between a pair of events.
+    The host issues one launch for all the steps, so short kernels are timed
+    back to back instead of at the host's launch rate.  Returns what
+    time_steps does (every step taken as the mean)."""
+    import torch
+    settle = {"seconds": 0.0, "steps": 0}
+    if settle_s > 0:
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(10):
+                run(stream)
+            n += 10
+            torch.cuda.synchronize()
+        settle = {"seconds": round(time.perf_counter() - t0, 3), "steps": n}
+    for _ in range(warmup):
+        run(stream)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream(device=stream.device)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for _ in range(steps):
+            run(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()  # untimed: the first replay uploads the graph
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if clock is not None:
+            clock.sample(0)
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        if clock is not None:
+            clock.sample(1)
+    torch.cuda.synchronize()
+    mean_ms = start.elapsed_time(end) / steps
+    return mean_ms, [mean_ms] * steps, settle
+
+
 def step_stats(mean_ms, ms_list):
     srt = sorted(ms_list)
     n = len(srt)
@@ -455,7 +498,7 @@ def copy_calibration(args) -> int:
     return 0
 
 
-def main() -> int:
+def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -464,6 +507,10 @@ def main() -> int:
                     help="seconds of repeated steps before the warm-up, so that the shader "
                          "clock reaches its loaded level (declared in the output; 0: none)")
     ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--graph", action="store_true",
+                    help="forward only: capture the timed steps once in a HIP graph and time "
+                         "one replay (short workloads are otherwise timed at the host's "
+                         "launch rate)")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "decode"), default="fwd",
                     help="time the forward pass (the headline), the backward pass, or "
                          "paged-cache decoding (workload default: " + DECODE_DEFAULT + ")")
@@ -475,12 +522,15 @@ def main() -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this "
                          "many MiB per step (reference for HBM byte counters)")
-    args = ap.parse_args()
+    args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the per-head work needs no exchange; see the sharding notes in the design "
               "document). Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.graph and args.pass_ != "fwd":
+        print("--graph times the forward pass only", file=sys.stderr)
         return 2
 
     import torch
@@ -528,9 +578,18 @@ def main() -> int:
                 raise fa.FaError(st, fa.fa_last_error())
 
     clock = ClockSampler(dev, stream)
-    mean_ms, times, settle = time_steps(step, stream, args.steps, args.warmup, args.settle_s,
-                                        clock)
-    stats = step_stats(mean_ms, times)
+    if args.graph:
+        def run(s):
+            fa.forward(q, k, v, mask=w.mask, window=window, scale=w.scale, out=o, lse=lse,
+                       stream=s)
+        mean_ms, times, settle = time_graph(run, stream, args.steps, args.warmup,
+                                            args.settle_s, clock)
+        stats = {"mean": round(mean_ms, 4),
+                 "note": "one graph replay of all the steps: no per-step times"}
+    else:
+        mean_ms, times, settle = time_steps(step, stream, args.steps, args.warmup,
+                                            args.settle_s, clock)
+        stats = step_stats(mean_ms, times)
     ms = mean_ms
     clk = clock.mean_mhz()
 
@@ -574,6 +633,8 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": traffic},
         "step_ms": stats,
+        "launch": ("graph: the timed steps captured once, one replay timed" if args.graph
+                   else "stream: one launch per step from the host"),
         "clock_settle": settle,
         "clock": clk,
         "hbm": {"compulsory_bytes": w.compulsory_bytes(),

@@ -39,6 +39,12 @@ def test_clock_library_refuses_bad_arguments_before_any_launch():
     assert lib.fa_mfma_ceiling(fake + 2, 8, 1, 1, 1, None) == -1
 
 
+def test_bench_graph_mode_is_forward_only():
+    # refused before anything touches a GPU
+    assert bench.main(["--graph", "--pass", "bwd"]) == 2
+    assert bench.main(["--graph", "--pass", "decode"]) == 2
+
+
 def _write_csv(path, header, rows):
     with open(path, "w", newline="") as f:
         w = csv.writer(f)
