@@ -58,7 +58,8 @@ def test_no_packed_fp32_arithmetic(asm, src):
     assert not bad, f"{src}: {bad[:3]}"
 
 
-@pytest.mark.parametrize("src", ["fa_fwd_mfma.hip", "fa_bwd_mfma.hip", "fa_decode.hip"])
+@pytest.mark.parametrize("src", ["fa_fwd_mfma.hip", "fa_bwd_mfma.hip", "fa_decode.hip",
+                                 "fa_fwd_f32.hip"])
 def test_no_scratch_spills(asm, src):
     sizes = [int(m.group(1)) for m in
              (re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", ln) for ln in asm[src]) if m]
