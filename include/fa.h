@@ -159,7 +159,7 @@ fa_status fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float
  *           its contents on return are those row terms.
  * Hkv     : >= 1 and dividing H (Hkv == H: multi-head attention).
  * Every other argument is read as by fa_fwd.  Supported: FA_F16 / FA_BF16
- * with d in {64, 128}.  fp32 products are accumulated in fp32 and each
+ * with d in {64, 128, 256}.  fp32 products are accumulated in fp32 and each
  * gradient is rounded to nearest-even into `dtype` once, at the end.
  *
  * Ownership, stream order and determinism are as for fa_fwd (three kernel
@@ -170,7 +170,7 @@ fa_status fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float
  *                   1 with FA_MASK_WINDOW; a scale rejected as by fa_fwd; any of dq, dk,
  *                   dv, delta overlapping an input or another of them; byte
  *                   counts that overflow, or one head larger than 2 GiB.
- *   FA_EUNSUPPORTED FA_F32, or d outside {64, 128}.
+ *   FA_EUNSUPPORTED FA_F32, or d outside {64, 128, 256}.
  *   FA_EHIP         a launch failed; fa_last_error() holds the HIP message.
  */
 fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,

@@ -240,9 +240,12 @@ fa_status bwd_impl(const void *q, const void *k, const void *v, const void *o, c
   const fa::DType dt = dtype == FA_BF16 ? fa::kBF16 : fa::kF16;
   if (dtype == FA_F32 || !fa::mfma_backward(dt, (int)d, eff_mask, &a, nullptr, false, &info, &err))
     return fail(FA_EUNSUPPORTED, "no backward kernel for dtype=%s d=%lld (supported: bf16/f16 "
-                "with d in {64,128})", dtype_name(dtype), (long long)d);
+                "with d in {64,128,256})", dtype_name(dtype), (long long)d);
   const int64_t nt = (S + info.block_rows - 1) / info.block_rows;
-  if (nt * bh > (int64_t)INT32_MAX || rows / 16 + 1 > (int64_t)INT32_MAX)
+  // at d = 256 two dK/dV work-groups share each key tile; the row-term
+  // kernel takes 2048 / d rows per work-group
+  if (nt * bh * (d == 256 ? 2 : 1) > (int64_t)INT32_MAX ||
+      rows / (2048 / d) + 1 > (int64_t)INT32_MAX)
     return fail(FA_EINVAL, "grid too large");
 
   if (log_enabled())

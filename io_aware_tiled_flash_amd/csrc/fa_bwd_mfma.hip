@@ -57,13 +57,14 @@ __device__ inline void load_rows_tile(u32x4 rsrc, int row0, u32x4 *lds_tile, int
 }
 
 // Store a transposed accumulator (lane: one column index `col` of the
-// output rows, registers: d values 32*db + 8*(r/4) + 4*lg + (r%4)) as the
-// row `col` of a [rows][D] slab, RNE to the element type.
-template <class Ty, int D>
-__device__ inline void store_rowmajor(uint16_t *row_ptr, const f32x16 (&acc)[D / 32], float mul,
+// output rows, registers: d values 32*db + 8*(r/4) + 4*lg + (r%4), NB
+// blocks) as 32*NB values of the row `col` of a row-major slab, starting at
+// row_ptr, RNE to the element type.
+template <class Ty, int NB>
+__device__ inline void store_rowmajor(uint16_t *row_ptr, const f32x16 (&acc)[NB], float mul,
                                       int lg) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < NB; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x2 w;
@@ -98,7 +99,13 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: one work-group per 32*NW keys of one key/value head.
+// dK and dV: one work-group per 32*NW keys of one key/value head and
+// 1/DSPLIT of the head dimension.  With DSPLIT = 2 (d = 256, where whole-d
+// accumulators do not fit beside the K and V operands) the two work-groups of
+// a key tile both compute S and dP over the whole d and each accumulates dK
+// and dV for its half of the columns: 1.5 times the matrix work of whole-d
+// accumulation, and the same query stream read twice (the two work-groups
+// are adjacent in launch order, so the second read mostly hits L2).
 //
 // Software pipeline over the query tiles u of the work-group's stream (one
 // wave, 32 keys; the same for every wave):
@@ -116,11 +123,11 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdArgs a) {
 // buffer choice is a compile-time constant.  Tiles past the end of the
 // stream read out of range (zero fill) and contribute nothing: with Q and
 // dO zero, dP, D and dO^T P all vanish.
-template <class Ty, int D, int MASK, int NW>
+template <class Ty, int D, int MASK, int NW, int DSPLIT>
 __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BKV = 32 * NW;  // keys per work-group
   constexpr int BQ = 32;        // query rows per streamed tile
-  constexpr int NKS = D / 16, NDB = D / 32, KCH = D / 8;
+  constexpr int NKS = D / 16, NDB = D / 32 / DSPLIT, KCH = D / 8;  // NDB: d blocks owned
   constexpr int TILE_CHUNKS = BQ * KCH;
   constexpr int LPW = TILE_CHUNKS / 64 / NW;       // 16-byte loads per wave per tile and tensor
   constexpr int LOADS = 2 * LPW + 1;               // per wave per tile (Q, dO, one statistic)
@@ -139,7 +146,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int S = a.S, H = a.H, Hkv = a.Hkv, group = H / Hkv;
   const int n_kv = a.B * Hkv;
   const int kvi = blockIdx.x % n_kv;  // key/value head (b * Hkv + hk)
-  const int kt = blockIdx.x / n_kv;   // key tile; the first ones see the most rows
+  const int kt = blockIdx.x / n_kv / DSPLIT;  // key tile; the first ones see the most rows
+  const int dh = (blockIdx.x / n_kv) % DSPLIT;  // part of d owned: columns 32*NDB*dh ...
   const int b = kvi / Hkv, hk = kvi - b * Hkv;
   const int k0 = kt * BKV, kw0 = k0 + 32 * wave;
   const float c = a.scale_log2;
@@ -171,7 +179,13 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int nq = max(qt_end - qt_begin, 0);
   const int total = group * nq;  // (query head of the group, query tile) pairs
 
-  const TileOffsets<D> off(lane);
+  TileOffsets<D> off(lane);
+  // transposed operands address this work-group's columns 32*NDB*dh ...
+  // (a multiple of 128 columns: the swizzle permutes only the low 16 chunks)
+  if (DSPLIT > 1) {
+#pragma unroll
+    for (int j = 0; j < TileOffsets<D>::NVB; ++j) off.tr_base[j] += 64 * NDB * dh;
+  }
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dkacc[i] = dvacc[i] = f32x16{};
@@ -274,16 +288,24 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     const char *dp = (const char *)&do_lds[prev][0];
     set_src();
     // ---- phase 1: S(u), dP(u) | dS(u-1) ----
+    // Row terms D of tile u-1, four at a time; at d = 256 each group is read
+    // a few steps before its first use rather than all up front, which keeps
+    // the registers within the file.
     float dl[16];
-    if (HAS_PREV) {
+    auto load_dl = [&](int q4) __attribute__((always_inline)) {
+      const float4 d4 = *(const float4 *)&stat_lds[prev][1][8 * q4 + 4 * lg];
+      dl[4 * q4 + 0] = d4.x;
+      dl[4 * q4 + 1] = d4.y;
+      dl[4 * q4 + 2] = d4.z;
+      dl[4 * q4 + 3] = d4.w;
+    };
+    constexpr bool LATE_DL = D == 256;
+    // first phase-1 step that uses group q4, and the step that reads it
+    auto dl_use = [](int q4) constexpr { return ((4 * q4 + 1) * NS1 + 15) / 16 - 1; };
+    auto dl_read = [&](int q4) constexpr { return dl_use(q4) > 4 ? dl_use(q4) - 4 : 0; };
+    if (HAS_PREV && !LATE_DL) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 d4 = *(const float4 *)&stat_lds[prev][1][8 * q4 + 4 * lg];
-        dl[4 * q4 + 0] = d4.x;
-        dl[4 * q4 + 1] = d4.y;
-        dl[4 * q4 + 2] = d4.z;
-        dl[4 * q4 + 3] = d4.w;
-      }
+      for (int q4 = 0; q4 < 4; ++q4) load_dl(q4);
     }
     u32x4 rop[RPD + 1];
     auto read_row = [&](int st) __attribute__((always_inline)) {
@@ -308,6 +330,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int d = 0; d < LOADS; ++d)
         if ((d * NS1) / LOADS == st) dma(ldst, d);
+      if (HAS_PREV && LATE_DL) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          if (dl_read(q4) == st) load_dl(q4);
+      }
       if (HAS_PREV) {
 #pragma unroll
         for (int r = st * 16 / NS1; r < (st + 1) * 16 / NS1; ++r) {
@@ -414,11 +441,13 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     step(I1{}, T{}, F{}, n_main + 1);
   }
 
-  // dK = scale * dS^T Q; each lane holds d values of key kw0 + lq.
+  // dK = scale * dS^T Q; each lane holds this work-group's d values of key
+  // kw0 + lq.
   const int key = kw0 + lq;
   if (key < S) {
-    store_rowmajor<Ty, D>((uint16_t *)a.dk + kv_off + (size_t)key * D, dkacc, a.scale, lg);
-    store_rowmajor<Ty, D>((uint16_t *)a.dv + kv_off + (size_t)key * D, dvacc, 1.f, lg);
+    const size_t o = kv_off + (size_t)key * D + 32 * NDB * dh;
+    store_rowmajor<Ty, NDB>((uint16_t *)a.dk + o, dkacc, a.scale, lg);
+    store_rowmajor<Ty, NDB>((uint16_t *)a.dv + o, dvacc, 1.f, lg);
   }
 }
 
@@ -648,7 +677,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
   }
 
   if (row < S)
-    store_rowmajor<Ty, D>((uint16_t *)a.dq + q_off + (size_t)row * D, dqacc, a.scale, lg);
+    store_rowmajor<Ty, D / 32>((uint16_t *)a.dq + q_off + (size_t)row * D, dqacc, a.scale, lg);
 }
 
 // ---------------------------------------------------------------------------
@@ -672,8 +701,10 @@ bool run_backward(const BwdArgs *a, hipStream_t stream, bool launch, LaunchInfo 
                          dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), kargs, 0, stream);
   if (*err != hipSuccess) return true;
   const int nkt = (a->S + 32 * NW - 1) / (32 * NW);
-  *err = hipLaunchKernel((const void *)&fa_bwd_dkdv_kernel<Ty, D, MASK, NW>,
-                         dim3((unsigned)(nkt * a->B * a->Hkv)), dim3(NW * 64), kargs, 0, stream);
+  constexpr int DSPLIT = D == 256 ? 2 : 1;
+  *err = hipLaunchKernel((const void *)&fa_bwd_dkdv_kernel<Ty, D, MASK, NW, DSPLIT>,
+                         dim3((unsigned)(nkt * DSPLIT * a->B * a->Hkv)), dim3(NW * 64), kargs, 0,
+                         stream);
   if (*err != hipSuccess) return true;
   *err = hipLaunchKernel((const void *)&fa_bwd_dq_kernel<Ty, D, MASK, NW>,
                          dim3((unsigned)(nkt * a->B * a->H)), dim3(NW * 64), kargs, 0, stream);
@@ -697,6 +728,7 @@ bool bwd_by_dim(int d, int mask, const BwdArgs *a, hipStream_t s, bool launch, L
   switch (d) {
     case 64: return bwd_by_mask<Ty, 64>(mask, a, s, launch, info, err);
     case 128: return bwd_by_mask<Ty, 128>(mask, a, s, launch, info, err);
+    case 256: return bwd_by_mask<Ty, 256>(mask, a, s, launch, info, err);
   }
   return false;
 }

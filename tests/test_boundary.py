@@ -201,8 +201,8 @@ def test_backward_invalid_arguments_are_rejected_before_any_launch(kw, needle):
     assert needle in fa.fa_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(dtype=0), dict(dtype=0, d=64), dict(d=256),
-                                dict(d=96, dtype=1), dict(d=32)])
+@pytest.mark.parametrize("kw", [dict(dtype=0), dict(dtype=0, d=64), dict(dtype=0, d=256),
+                                dict(d=512), dict(d=96, dtype=1), dict(d=32)])
 def test_backward_unsupported_configuration_is_an_error(kw):
     assert _call_bwd(**kw) == fa.FA_EUNSUPPORTED
     assert "no backward kernel" in fa.fa_last_error()

@@ -92,6 +92,11 @@ CASES = [
     ("f16", 64, "none", 6, 3, 257, None),
     ("bf16", 128, "causal", 4, 1, 200, None),   # one shared key/value head
     ("bf16", 128, "window", 4, 2, 333, 50),
+    # d = 256: two dK/dV work-groups per key tile, each owning half of d
+    ("bf16", 256, "causal", 2, 2, 300, None),
+    ("f16", 256, "none", 1, 1, 200, None),
+    ("bf16", 256, "window", 4, 2, 333, 70),
+    ("f16", 256, "causal", 4, 1, 129, None),
 ]
 
 
@@ -123,18 +128,22 @@ def test_backward_window_covering_sequence_is_causal_bitwise():
         assert torch.equal(x, y)
 
 
-def test_backward_deterministic_repeat():
-    q, k, v, do = _inputs(1, 4, 2, 400, 128, "bf16", 4)
+@pytest.mark.parametrize("d", [128, 256])
+def test_backward_deterministic_repeat(d):
+    q, k, v, do = _inputs(1, 4, 2, 400, d, "bf16", 4)
     a = _run(q, k, v, do, "causal", None, 0.09)
     b = _run(q, k, v, do, "causal", None, 0.09)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
 
-def test_backward_outputs_do_not_touch_neighbours():
+@pytest.mark.parametrize("d", [64, 256])
+def test_backward_outputs_do_not_touch_neighbours(d):
     """dq, dk, dv, delta carved out of larger buffers: the guard bytes around
-    each stay untouched."""
-    B, H, Hkv, S, d = 1, 2, 1, 200, 64
+    each stay untouched (at d = 256 each dK/dV work-group writes half of
+    every row)."""
+    _say(f"bwd guard bands d={d}")
+    B, H, Hkv, S = 1, 2, 1, 200
     q, k, v, do = _inputs(B, H, Hkv, S, d, "bf16", 5)
     dev = torch.device("cuda:0")
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
