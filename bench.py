@@ -49,10 +49,7 @@ HBM_PEAK_GBS = 8000.0
 BWD_FLOP_RATIO = 2.5
 # The backward's kernels issue 14*d FLOPs per visible pair (the dK/dV kernel
 # recomputes S and dP, and so does the dQ kernel): 1.4 times the credited 10*d.
-# At d = 256 both dK/dV work-groups of a key tile recompute S and dP over the
-# whole d (each accumulates half of dK and dV): 18*d, 1.8 times.
 BWD_ISSUED_RATIO = 1.4
-BWD_ISSUED_RATIO_D256 = 1.8
 BWD_KERNELS = ("fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel")
 GRAD_SEED_OFFSET = 7919  # dO is drawn with seed = the workload's seed + this
 DECODE_DEFAULT = "decode_opt13b_b256"
@@ -653,7 +650,7 @@ def main(argv=None) -> int:
         result["roofline"]["frac_at_measured_clock"] = round(tflops / peak_at, 4)
     issued_ratio = 1.0
     if bwd:
-        issued_ratio = BWD_ISSUED_RATIO_D256 if w.d == 256 else BWD_ISSUED_RATIO
+        issued_ratio = BWD_ISSUED_RATIO
         result["roofline"]["scope"] = "whole pass (three launches)"
         result["roofline"]["mfma_flop_issued_per_credited"] = issued_ratio
     if args.ceiling and w.dtype in ("bf16", "f16"):

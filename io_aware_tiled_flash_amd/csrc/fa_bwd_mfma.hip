@@ -99,13 +99,7 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: one work-group per 32*NW keys of one key/value head and
-// 1/DSPLIT of the head dimension.  With DSPLIT = 2 (d = 256, where whole-d
-// accumulators do not fit beside the K and V operands) the two work-groups of
-// a key tile both compute S and dP over the whole d and each accumulates dK
-// and dV for its half of the columns: 1.5 times the matrix work of whole-d
-// accumulation, and the same query stream read twice (the two work-groups
-// are adjacent in launch order, so the second read mostly hits L2).
+// dK and dV: one work-group per 32*NW keys of one key/value head.
 //
 // Software pipeline over the query tiles u of the work-group's stream (one
 // wave, 32 keys; the same for every wave):
@@ -123,11 +117,11 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdArgs a) {
 // buffer choice is a compile-time constant.  Tiles past the end of the
 // stream read out of range (zero fill) and contribute nothing: with Q and
 // dO zero, dP, D and dO^T P all vanish.
-template <class Ty, int D, int MASK, int NW, int DSPLIT>
+template <class Ty, int D, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BKV = 32 * NW;  // keys per work-group
   constexpr int BQ = 32;        // query rows per streamed tile
-  constexpr int NKS = D / 16, NDB = D / 32 / DSPLIT, KCH = D / 8;  // NDB: d blocks owned
+  constexpr int NKS = D / 16, NDB = D / 32, KCH = D / 8;
   constexpr int TILE_CHUNKS = BQ * KCH;
   constexpr int LPW = TILE_CHUNKS / 64 / NW;       // 16-byte loads per wave per tile and tensor
   constexpr int LOADS = 2 * LPW + 1;               // per wave per tile (Q, dO, one statistic)
@@ -146,8 +140,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int S = a.S, H = a.H, Hkv = a.Hkv, group = H / Hkv;
   const int n_kv = a.B * Hkv;
   const int kvi = blockIdx.x % n_kv;  // key/value head (b * Hkv + hk)
-  const int kt = blockIdx.x / n_kv / DSPLIT;  // key tile; the first ones see the most rows
-  const int dh = (blockIdx.x / n_kv) % DSPLIT;  // part of d owned: columns 32*NDB*dh ...
+  const int kt = blockIdx.x / n_kv;   // key tile; the first ones see the most rows
   const int b = kvi / Hkv, hk = kvi - b * Hkv;
   const int k0 = kt * BKV, kw0 = k0 + 32 * wave;
   const float c = a.scale_log2;
@@ -179,13 +172,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int nq = max(qt_end - qt_begin, 0);
   const int total = group * nq;  // (query head of the group, query tile) pairs
 
-  TileOffsets<D> off(lane);
-  // transposed operands address this work-group's columns 32*NDB*dh ...
-  // (a multiple of 128 columns: the swizzle permutes only the low 16 chunks)
-  if (DSPLIT > 1) {
-#pragma unroll
-    for (int j = 0; j < TileOffsets<D>::NVB; ++j) off.tr_base[j] += 64 * NDB * dh;
-  }
+  const TileOffsets<D> off(lane);
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dkacc[i] = dvacc[i] = f32x16{};
@@ -288,24 +275,16 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     const char *dp = (const char *)&do_lds[prev][0];
     set_src();
     // ---- phase 1: S(u), dP(u) | dS(u-1) ----
-    // Row terms D of tile u-1, four at a time; at d = 256 each group is read
-    // a few steps before its first use rather than all up front, which keeps
-    // the registers within the file.
     float dl[16];
-    auto load_dl = [&](int q4) __attribute__((always_inline)) {
-      const float4 d4 = *(const float4 *)&stat_lds[prev][1][8 * q4 + 4 * lg];
-      dl[4 * q4 + 0] = d4.x;
-      dl[4 * q4 + 1] = d4.y;
-      dl[4 * q4 + 2] = d4.z;
-      dl[4 * q4 + 3] = d4.w;
-    };
-    constexpr bool LATE_DL = D == 256;
-    // first phase-1 step that uses group q4, and the step that reads it
-    auto dl_use = [](int q4) constexpr { return ((4 * q4 + 1) * NS1 + 15) / 16 - 1; };
-    auto dl_read = [&](int q4) constexpr { return dl_use(q4) > 4 ? dl_use(q4) - 4 : 0; };
-    if (HAS_PREV && !LATE_DL) {
+    if (HAS_PREV) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) load_dl(q4);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 d4 = *(const float4 *)&stat_lds[prev][1][8 * q4 + 4 * lg];
+        dl[4 * q4 + 0] = d4.x;
+        dl[4 * q4 + 1] = d4.y;
+        dl[4 * q4 + 2] = d4.z;
+        dl[4 * q4 + 3] = d4.w;
+      }
     }
     u32x4 rop[RPD + 1];
     auto read_row = [&](int st) __attribute__((always_inline)) {
@@ -330,11 +309,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int d = 0; d < LOADS; ++d)
         if ((d * NS1) / LOADS == st) dma(ldst, d);
-      if (HAS_PREV && LATE_DL) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          if (dl_read(q4) == st) load_dl(q4);
-      }
       if (HAS_PREV) {
 #pragma unroll
         for (int r = st * 16 / NS1; r < (st + 1) * 16 / NS1; ++r) {
@@ -441,11 +415,375 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     step(I1{}, T{}, F{}, n_main + 1);
   }
 
-  // dK = scale * dS^T Q; each lane holds this work-group's d values of key
-  // kw0 + lq.
+  // dK = scale * dS^T Q; each lane holds d values of key kw0 + lq.
   const int key = kw0 + lq;
   if (key < S) {
-    const size_t o = kv_off + (size_t)key * D + 32 * NDB * dh;
+    store_rowmajor<Ty, NDB>((uint16_t *)a.dk + kv_off + (size_t)key * D, dkacc, a.scale, lg);
+    store_rowmajor<Ty, NDB>((uint16_t *)a.dv + kv_off + (size_t)key * D, dvacc, 1.f, lg);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV by wave pairs: one work-group per 32*NP keys of one key/value
+// head, 2*NP waves.  The two waves of a pair own the same 32 keys: the first
+// (role 0) keeps their K rows in registers and computes S = Q K^T, the
+// second (role 1) keeps their V rows and computes dP = dO V^T, each over the
+// whole d.  Role 0 turns S into the weights P, role 1 turns dP into
+// X = dP - D; each writes its fp32 tile to LDS and reads its partner's, both
+// form dS = P * X, and each accumulates dV += dO^T P and dK += Q^T dS for its
+// half of the columns.  A pair's matrix work per tile is the four products
+// once (no recomputation) and each wave holds one of K, V and half of the
+// accumulators, which is what lets the head width reach 256.
+//
+// The pipeline is the whole-d kernel's: phase 1 of step u runs the S(u) or
+// dP(u) chain beside dS(u-1) and its packing, phase 2 runs dV and dK of tile
+// u-1 beside the wave's own P(u) or X(u), written to the exchange buffer at
+// the end of the step.  The tile loop is compiled once per role, so every
+// LDS offset is a compile-time constant.  With XB = 2 exchange buffers (by
+// tile parity) the step's one barrier orders each write after the partner's
+// read of the same buffer; with XB = 1 (where LDS holds only one) a second
+// barrier after phase 1 does.
+template <class Ty, int D, int MASK, int NP, int XB>
+__global__ __launch_bounds__(NP * 128, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
+  constexpr int NW = 2 * NP;      // waves
+  constexpr int BKV = 32 * NP;    // keys per work-group
+  constexpr int BQ = 32;          // query rows per streamed tile
+  constexpr int NKS = D / 16, NDB = D / 64, KCH = D / 8;  // NDB: d blocks per role
+  constexpr int TILE_CHUNKS = BQ * KCH;
+  constexpr int LPW = TILE_CHUNKS / 64 / NW;  // 16-byte loads per wave per tile and tensor
+  constexpr int LOADS = 2 * LPW + 1;          // per wave per tile (Q, dO, one statistic)
+  constexpr int NST = 4, PF = 2, RPD = 3;
+  constexpr int NS1 = NKS;                    // phase-1 MFMAs (S or dP)
+  constexpr int NS2 = 4 * NDB;                // phase-2 MFMAs (dV and dK, 2 key halves)
+  static_assert(TILE_CHUNKS % (64 * NW) == 0, "tile must split evenly over the waves");
+  // [tensor: Q, dO][stage]: the dO stages follow the Q stages
+  __shared__ u32x4 tiles[2][NST][TILE_CHUNKS];
+  __shared__ float stat_lds[NST][2][64];      // [stage][LSE, D][row]
+  // [buffer][pair][role][part][lane]: a wave's 16 fp32 values per lane, in
+  // four parts of four, part-major so that one part is 1 KB of consecutive
+  // lanes
+  __shared__ f32x4 x_lds[XB][NP][2][4][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave % NP, role = wave / NP;
+  const int lq = lane & 31, lg = lane >> 5;
+  const int S = a.S, H = a.H, Hkv = a.Hkv, group = H / Hkv;
+  const int n_kv = a.B * Hkv;
+  const int kvi = blockIdx.x % n_kv;  // key/value head (b * Hkv + hk)
+  const int kt = blockIdx.x / n_kv;   // key tile; the first ones see the most rows
+  const int b = kvi / Hkv, hk = kvi - b * Hkv;
+  const int k0 = kt * BKV, kw0 = k0 + 32 * pair;
+  const float c = a.scale_log2;
+
+  const size_t kv_off = (size_t)kvi * (size_t)S * D;
+  const uint32_t head_bytes = (uint32_t)S * D * 2u;
+  // This wave's keys as the B operand of its product: lane (key kw0 + lq,
+  // group lg) holds row chunk 2*ks + lg of K (role 0) or V (role 1).
+  const __amdgpu_buffer_rsrc_t rkv =
+      make_rsrc((const uint16_t *)(role ? a.v : a.k) + kv_off, head_bytes);
+  u32x4 kvreg[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    kvreg[ks] = load16(rkv, (uint32_t)((kw0 + lq) * D + 16 * ks + 8 * lg) * 2u);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(kvreg[ks]));
+
+  // Query tiles that can see a key of this work-group.
+  const int nqt_all = (S + BQ - 1) / BQ;
+  int qt_begin = 0, qt_end = nqt_all;
+  if (MASK != kMaskNone) qt_begin = k0 / BQ;  // rows i >= key
+  if (MASK == kMaskWindow) {
+    const int last_row = min(S - 1, k0 + BKV - 1 + a.window - 1);  // i < key + window
+    qt_end = min(qt_end, last_row / BQ + 1);
+  }
+  const int nq = max(qt_end - qt_begin, 0);
+  const int total = group * nq;  // (query head of the group, query tile) pairs
+
+  const TileOffsets<D> off(lane);
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dkacc[i] = dvacc[i] = f32x16{};
+
+  // Stream cursors, as in the whole-d kernel.
+  struct Cursor {
+    int j, qt;
+  };
+  auto advance = [&](Cursor &cu) __attribute__((always_inline)) {
+    const bool wrap = cu.qt + 1 == qt_end;
+    cu.qt = wrap ? qt_begin : cu.qt + 1;
+    cu.j += wrap ? 1 : 0;
+  };
+  auto row0_of = [&](const Cursor &cu) __attribute__((always_inline)) {
+    return cu.j < group ? cu.qt * BQ : S + BQ;
+  };
+  Cursor ld{0, qt_begin}, fin{0, qt_begin};
+  struct Src {
+    u32x4 q, dout, stat;
+    int row0;
+  } src;
+  auto set_src = [&]() __attribute__((always_inline)) {
+    const int bh = b * H + hk * group + (ld.j < group ? ld.j : 0);
+    const size_t q_off = (size_t)bh * (size_t)S * D;
+    src.q = rsrc_words((const uint16_t *)a.q + q_off, head_bytes);
+    src.dout = rsrc_words((const uint16_t *)a.dout + q_off, head_bytes);
+    // waves 0 and 1 load LSE and D; the others load the same rows again into
+    // the same slots (identical bytes), which keeps every wave's load count
+    // equal for the counted waits
+    const float *st = (wave & 1) ? a.delta : a.lse;
+    src.stat = rsrc_words(st + (size_t)bh * S, (uint32_t)S * 4u);
+    src.row0 = row0_of(ld);
+  };
+  auto dma = [&](int st, int d) __attribute__((always_inline)) {
+    if (d < 2 * LPW) {
+      const int i = d % LPW;
+      const int blk = wave * LPW + i;
+      const int pos = 64 * blk + lane;
+      const int r = pos / KCH, cc = swz<D>(r, pos % KCH);
+      const uint32_t o = (uint32_t)((src.row0 + r) * D + 8 * cc) * 2u;
+      if (d < LPW)
+        load16_to_lds(src.q, o, (uint32_t)(uintptr_t)&tiles[0][st][64 * blk]);
+      else
+        load16_to_lds(src.dout, o, (uint32_t)(uintptr_t)&tiles[1][st][64 * blk]);
+    } else {
+      load4_to_lds(src.stat, (uint32_t)(src.row0 + lane) * 4u,
+                   (uint32_t)(uintptr_t)&stat_lds[st][wave & 1][0]);
+    }
+  };
+
+  // Pipeline registers: the product of the current tile (S or dP), the
+  // wave's own fp32 values of the newest tile (P or X), packed P and dS of
+  // the previous tile.
+  f32x16 acc1;
+  float own[16];
+  u32x4 ppk[2], dspk[2];
+  // this pair's exchange slots from (pair, role 0, part 0, lane)
+  FA_LDS f32x4 *const x_lane =
+      (FA_LDS f32x4 *)(uintptr_t)(uint32_t)(uintptr_t)&x_lds[0][pair][0][0][lane];
+
+  auto edge_of = [&](int row0) __attribute__((always_inline)) {
+    if (MASK == kMaskNone) return false;
+    bool e = row0 < kw0 + 31;
+    if (MASK == kMaskWindow) e = e || row0 + BQ - 1 > kw0 - 1 + a.window;
+    return e;
+  };
+
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+    constexpr int R = decltype(role_c)::value;
+    // slot (buffer xb, role rr, part q4) of this pair and lane
+    auto x_at = [&](int xb, int rr, int q4) __attribute__((always_inline)) {
+      return x_lane + ((xb * NP * 2 + rr) * 4 + q4) * 64;
+    };
+    // Per-lane operand offsets: this role's row operand (Q for role 0, dO
+    // for role 1), and the transposed Q and dO operands of its half of the
+    // columns.  Where the dO stages lie beyond the 16-bit immediate of the
+    // LDS reads (FAR, d = 256), the role's offsets carry the distance from
+    // the Q stages so that every stage and step offset stays an immediate;
+    // otherwise the tile pointers carry it and the offsets are the common
+    // ones.
+    constexpr int TSZ = (int)sizeof(tiles[0]);
+    constexpr bool FAR = 2 * TSZ > 65536;
+    int rb[TileOffsets<D>::KSW], tq[TileOffsets<D>::NVB], td[TileOffsets<D>::NVB];
+#pragma unroll
+    for (int j = 0; j < TileOffsets<D>::KSW; ++j) rb[j] = off.row_base[j] + (FAR ? R * TSZ : 0);
+#pragma unroll
+    for (int j = 0; j < TileOffsets<D>::NVB; ++j) {
+      tq[j] = off.tr_base[j] + (FAR ? 64 * NDB * R : 0);
+      td[j] = tq[j] + (FAR ? TSZ : 0);
+    }
+    auto row_op = [&](const char *tile, int ks) __attribute__((always_inline)) {
+      constexpr int KSW = TileOffsets<D>::KSW;
+      return *(const u32x4 *)(tile + rb[ks % KSW] + 16 * 2 * KSW * (ks / KSW));
+    };
+    auto tr_op = [&](const char *tile, const int (&base)[TileOffsets<D>::NVB], int kk, int db)
+                     __attribute__((always_inline)) {
+      u32x4 op;
+#pragma unroll
+      for (int i2 = 0; i2 < 2; ++i2) {
+        const u32x2 v2 = lds_read_tr16((const FA_LDS void *)(tile + base[2 * (db & 3) + i2] +
+                                                             16 * kk * (D * 2) + 64 * (db & ~3)));
+        op[2 * i2] = v2[0];
+        op[2 * i2 + 1] = v2[1];
+      }
+      return op;
+    };
+    auto step = [&](auto phase_c, auto has_prev_c, auto has_cur_c)
+                    __attribute__((always_inline)) {
+      constexpr int P = decltype(phase_c)::value;
+      constexpr bool HAS_PREV = decltype(has_prev_c)::value,
+                     HAS_CUR = decltype(has_cur_c)::value;
+      constexpr int cur = P, prev = (P + NST - 1) % NST, ldst = (P + PF) % NST;
+      constexpr int xw = XB == 2 ? (P & 1) : 0, xr = XB == 2 ? ((P + 1) & 1) : 0;
+      const char *rc = (const char *)&tiles[FAR ? 0 : R][cur][0];
+      const char *qpc = (const char *)&tiles[0][prev][0] + (FAR ? 0 : 64 * NDB * R);
+      const char *dpc = (const char *)&tiles[FAR ? 0 : 1][prev][0] + (FAR ? 0 : 64 * NDB * R);
+      set_src();
+      // ---- phase 1: S(u) or dP(u) | dS(u-1) ----
+      float xv[16];
+      if (HAS_PREV) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v4 = *x_at(xr, 1 - R, q4);
+          xv[4 * q4 + 0] = v4.x;
+          xv[4 * q4 + 1] = v4.y;
+          xv[4 * q4 + 2] = v4.z;
+          xv[4 * q4 + 3] = v4.w;
+        }
+      }
+      u32x4 rop[RPD + 1];
+      if (HAS_CUR) {
+#pragma unroll
+        for (int st = 0; st < RPD; ++st) rop[st] = row_op(rc, st);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < NS1; ++st) {
+        if (HAS_CUR) {
+          if (st + RPD < NS1) rop[(st + RPD) % (RPD + 1)] = row_op(rc, st + RPD);
+          acc1 = Ty::mfma(rop[st % (RPD + 1)], kvreg[st], st == 0 ? f32x16{} : acc1);
+        }
+#pragma unroll
+        for (int d = 0; d < LOADS; ++d)
+          if ((d * NS1) / LOADS == st) dma(ldst, d);
+        if (HAS_PREV) {
+          // dS = P * X (the same product on both waves); P is the own
+          // values on role 0 and the partner's on role 1
+#pragma unroll
+          for (int r = st * 16 / NS1; r < (st + 1) * 16 / NS1; ++r) {
+            const float p = R == 0 ? own[r] : xv[r];
+            const float ds = own[r] * xv[r];
+            own[r] = ds;
+            xv[r] = p;
+            if (r & 1) {
+              dspk[r >> 3][(r & 7) >> 1] = Ty::pack2(own[r - 1], ds);
+              ppk[r >> 3][(r & 7) >> 1] = Ty::pack2(xv[r - 1], p);
+              pin(dspk[r >> 3][(r & 7) >> 1]);
+              pin(ppk[r >> 3][(r & 7) >> 1]);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (XB == 1 && HAS_PREV && HAS_CUR) {
+        // every wave has read the exchange buffer (the reads were consumed
+        // above) before any rewrites it
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      // ---- phase 2: dV, dK of tile u-1 | own values of tile u ----
+      float sv[16];
+      if (HAS_CUR) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 s4 = *(const float4 *)&stat_lds[cur][R][8 * q4 + 4 * lg];
+          const float m = R == 0 ? LOG2E : 1.f;
+          sv[4 * q4 + 0] = s4.x * m;
+          sv[4 * q4 + 1] = s4.y * m;
+          sv[4 * q4 + 2] = s4.z * m;
+          sv[4 * q4 + 3] = s4.w * m;
+        }
+      }
+      // step st: key half kk = st / (2*NDB), d block db = (st / 2) % NDB,
+      // dV (even st) or dK (odd st)
+      u32x4 top[RPD + 1];
+      auto read_tr = [&](int st) __attribute__((always_inline)) {
+        const int kk = st / (2 * NDB), db = (st >> 1) % NDB;
+        return (st & 1) ? tr_op(qpc, tq, kk, db) : tr_op(dpc, td, kk, db);
+      };
+      if (HAS_PREV) {
+#pragma unroll
+        for (int st = 0; st < RPD; ++st) top[st] = read_tr(st);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < NS2; ++st) {
+        if (HAS_PREV) {
+          if (st + RPD < NS2) top[(st + RPD) % (RPD + 1)] = read_tr(st + RPD);
+          const int kk = st / (2 * NDB), db = (st >> 1) % NDB;
+          if (st & 1)
+            dkacc[db] = Ty::mfma(top[st % (RPD + 1)], dspk[kk], dkacc[db]);
+          else
+            dvacc[db] = Ty::mfma(top[st % (RPD + 1)], ppk[kk], dvacc[db]);
+        }
+        if (HAS_CUR) {
+#pragma unroll
+          for (int r = st * 16 / NS2; r < (st + 1) * 16 / NS2; ++r)
+            own[r] = R == 0 ? __builtin_amdgcn_exp2f(fmaf(acc1[r], c, -sv[r])) : acc1[r] - sv[r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      advance(ld);
+      if (HAS_CUR) {
+        if (R == 0 && MASK != kMaskNone) {
+          // row = row0 + 4*lg + off(r): key <= row is off(r) >= t, and under
+          // a window key > row - window is off(r) < t + window
+          const int row0 = row0_of(fin);
+          if (edge_of(row0)) {
+            const int t = kw0 + lq - row0 - 4 * lg;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int o = 8 * (r >> 2) + (r & 3);
+              bool vis = o >= t;
+              if (MASK == kMaskWindow) vis = vis && o < t + a.window;
+              if (!vis) own[r] = 0.f;
+            }
+          }
+        }
+        advance(fin);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *x_at(xw, R, q4) = f32x4{own[4 * q4], own[4 * q4 + 1], own[4 * q4 + 2],
+                                   own[4 * q4 + 3]};
+      }
+      // Tile u+1 has landed once only tile u+PF's loads are outstanding; the
+      // exchange writes are complete before the barrier publishes them.
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS * (PF - 1)) : "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using T = std::true_type;
+    using F = std::false_type;
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      set_src();
+#pragma unroll
+      for (int d = 0; d < LOADS; ++d) dma(u, d);
+      advance(ld);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (PF - 1)) : "memory");
+    __builtin_amdgcn_s_barrier();
+    step(I0{}, F{}, T{});
+    const int n_main = (total - 1 + NST - 1) / NST * NST;
+    for (int u = 1; u <= n_main; u += NST) {
+      step(I1{}, T{}, T{});
+      step(I2{}, T{}, T{});
+      step(I3{}, T{}, T{});
+      step(I0{}, T{}, T{});
+    }
+    step(I1{}, T{}, F{});
+  };
+
+  // Settle the bookkeeping of the kernel-argument scalar loads before the
+  // loop (see the forward kernel).
+  asm volatile("" ::"s"(a.q), "s"(a.dout), "s"(a.lse), "s"(a.delta));
+  if (total > 0) {
+    if (role == 0)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
+  }
+
+  // dK = scale * dS^T Q; each lane holds this wave's half of the d values of
+  // key kw0 + lq.
+  const int key = kw0 + lq;
+  if (key < S) {
+    const size_t o = kv_off + (size_t)key * D + 32 * NDB * role;
     store_rowmajor<Ty, NDB>((uint16_t *)a.dk + o, dkacc, a.scale, lg);
     store_rowmajor<Ty, NDB>((uint16_t *)a.dv + o, dvacc, 1.f, lg);
   }
@@ -701,10 +1039,18 @@ bool run_backward(const BwdArgs *a, hipStream_t stream, bool launch, LaunchInfo 
                          dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), kargs, 0, stream);
   if (*err != hipSuccess) return true;
   const int nkt = (a->S + 32 * NW - 1) / (32 * NW);
-  constexpr int DSPLIT = D == 256 ? 2 : 1;
-  *err = hipLaunchKernel((const void *)&fa_bwd_dkdv_kernel<Ty, D, MASK, NW, DSPLIT>,
-                         dim3((unsigned)(nkt * DSPLIT * a->B * a->Hkv)), dim3(NW * 64), kargs, 0,
-                         stream);
+  if constexpr (D == 256) {
+    // wave pairs, 64 keys per work-group; LDS holds one exchange buffer
+    constexpr int NP = 2;
+    const int nkt_p = (a->S + 32 * NP - 1) / (32 * NP);
+    *err = hipLaunchKernel((const void *)&fa_bwd_dkdv_pair_kernel<Ty, D, MASK, NP, 1>,
+                           dim3((unsigned)(nkt_p * a->B * a->Hkv)), dim3(NP * 128), kargs, 0,
+                           stream);
+  } else {
+    *err = hipLaunchKernel((const void *)&fa_bwd_dkdv_kernel<Ty, D, MASK, NW>,
+                           dim3((unsigned)(nkt * a->B * a->Hkv)), dim3(NW * 64), kargs, 0,
+                           stream);
+  }
   if (*err != hipSuccess) return true;
   *err = hipLaunchKernel((const void *)&fa_bwd_dq_kernel<Ty, D, MASK, NW>,
                          dim3((unsigned)(nkt * a->B * a->H)), dim3(NW * 64), kargs, 0, stream);
