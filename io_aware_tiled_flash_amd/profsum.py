@@ -179,13 +179,22 @@ def cmd_sq(a) -> list[str]:
             note = ("  (not a clock: for a dispatch this short the GPU-busy count covers"
                     " more than the kernel's own span)")
         out.append(f"  clock_GHz (GRBM_GUI_ACTIVE / 8 dies / dispatch time): {ghz:.3f}{note}")
-    flops = w.flops()
+    # the kernel's own products per visible pair, 2 d FLOPs each: the forward's
+    # S and P V; the backward's dK/dV kernel S, dP, dV, dK; its dQ kernel S,
+    # dP, dQ
+    products = (("fa_bwd_dkdv", 4, "S, dP, dV, dK"), ("fa_bwd_dq", 3, "S, dP, dQ"))
+    n_prod, prod_names = 2, "S, P V"
+    for key, n, names in products:
+        if key in a.kernel:
+            n_prod, prod_names = n, names
+    flops = w.flops() * n_prod / 2
     if "SQ_INSTS_MFMA" in vals:
         mf = vals["SQ_INSTS_MFMA"]
         per = MFMA_FLOPS[a.mfma]
         out.append(f"  mfma_instructions: {mf:.6g}  x {per} flop = {mf * per:.4g} flop issued")
-        out.append(f"  algorithmic_flop (4 d per visible pair): {flops:.4g}")
-        out.append(f"  issued / algorithmic: {mf * per / flops:.4f} (the excess is masked work "
+        out.append(f"  algorithmic_flop ({2 * n_prod} d per visible pair: {prod_names}): "
+                   f"{flops:.4g}")
+        out.append(f"  issued / algorithmic: {mf * per / flops:.4f} (any excess is masked work "
                    f"on tiles that straddle a band edge or lie outside a wave's band)")
     if "SQ_WAVES" in vals and "SQ_WAVE_CYCLES" in vals:
         waves = vals["SQ_WAVES"]
