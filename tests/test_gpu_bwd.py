@@ -167,13 +167,12 @@ def test_backward_outputs_do_not_touch_neighbours(d):
         assert torch.equal(b[pad:pad + n].view_as(r), r)
 
 
-@pytest.fixture(scope="module")
-def full_size_backward():
-    """The benchmark's backward configuration at full size, run once on the
-    GPU for the tests below (inputs and gradients on the host)."""
+def _full_size(name):
+    """One bench backward configuration at full size, run once on the GPU
+    (inputs and gradients returned on the host)."""
     from workloads import WORKLOADS
 
-    w = WORKLOADS["prefill_8k_d128"]
+    w = WORKLOADS[name]
     _say(f"bwd full-size {w.name}: launching")
     q, k, v = make_inputs(w.B, w.H, w.S, w.d, w.dtype, w.seed, w.sigma, w.outliers, w.kv_heads)
     do = make_grad(w.B, w.H, w.S, w.d, w.dtype, w.seed + 7919)
@@ -186,13 +185,26 @@ def full_size_backward():
     return w, (q, k, v, do), (dq.cpu(), dk.cpu(), dv.cpu()), lse.cpu()
 
 
-def test_backward_full_size_identity(full_size_backward):
+@pytest.fixture(scope="module")
+def full_size_backward():
+    """The headline shape's backward (prefill_8k_d128) at full size."""
+    return _full_size("prefill_8k_d128")
+
+
+@pytest.fixture(scope="module")
+def full_size_backward_d256():
+    """The d = 256 backward workload (full_d256_f16: the wave-pair dK/dV
+    kernel) at full size."""
+    return _full_size("full_d256_f16")
+
+
+def _identity(full):
     """Every head: sum_j dV[j] = sum_i dO[i] (each row's probabilities sum to
     one), within the sum of the per-element bounds, which for this identity
     needs only dO and dV."""
     from bwd_bounds import UNIT, F32
 
-    w, (q, k, v, do), (dq, dk, dv), lse = full_size_backward
+    w, (q, k, v, do), (dq, dk, dv), lse = full
     for name_, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.isfinite(t.float()).all(), f"{name_} not finite"
     u = UNIT[w.dtype]
@@ -210,14 +222,14 @@ def test_backward_full_size_identity(full_size_backward):
             tol = (u + g + rho) * do64[b, heads].abs().sum(dim=(0, 1)) \
                 + u * dv64[b, gh].abs().sum(dim=0)
             gap = ((lhs - rhs).abs() / tol).max().item()
-            assert gap <= 1.0, f"kv head {gh}: sum_j dV - sum_i dO reaches {gap:.3f} of bound"
+            assert gap <= 1.0, (f"batch {b} kv head {gh}: sum_j dV - sum_i dO reaches "
+                                f"{gap:.3f} of bound")
 
 
-@pytest.mark.parametrize("first", [0, 8, 16, 24])
-def test_backward_full_size_every_element(full_size_backward, first):
-    """Heads first .. first+7 of the full-size backward: every element of dQ,
-    dK and dV against the oracle's exact gradients, within its bound.  The
-    heads run on a thread pool (the oracle's numpy work releases the GIL)."""
+def _every_element(full, pairs):
+    """The (batch, head) slices in pairs: every element of dQ, dK and dV
+    against the oracle's exact gradients, within its bound.  The slices run
+    on a thread pool (the oracle's numpy work releases the GIL)."""
     import os
     from concurrent.futures import ThreadPoolExecutor
 
@@ -226,25 +238,50 @@ def test_backward_full_size_every_element(full_size_backward, first):
     from bwd_bounds import UNIT, head_bounds
     from oracle import attention_bwd_rows_ref
 
-    w, (q, k, v, do), (dq, dk, dv), _ = full_size_backward
+    w, (q, k, v, do), (dq, dk, dv), _ = full
     assert w.kv_heads == w.H, "the whole-head check assumes one query head per kv head"
     u = UNIT[w.dtype]
 
-    def one(h):
-        args = (q[0, h], k[0, h], v[0, h], do[0, h], w.mask, w.window or None, w.scale)
+    def one(bh):
+        b, h = bh
+        args = (q[b, h], k[b, h], v[b, h], do[b, h], w.mask, w.window or None, w.scale)
         ref = attention_bwd_rows_ref(*args)
         bnd = head_bounds(*args, w.dtype)
         out = []
-        for got, r, e in zip((dq[0, h], dk[0, h], dv[0, h]), ref, bnd):
+        for got, r, e in zip((dq[b, h], dk[b, h], dv[b, h]), ref, bnd):
             out.append(excess(got, r, e + u * np.abs(r)))
         return out
 
-    heads = list(range(first, min(first + 8, w.H)))
-    _say(f"bwd full-size: heads {heads[0]}..{heads[-1]}, exact gradients and bounds")
+    _say(f"bwd full-size {w.name}: (batch, head) {pairs[0]}..{pairs[-1]}, exact gradients "
+         f"and bounds")
     workers = max(1, min(8, os.cpu_count() or 1))
     with threadpool_limits(limits=2), ThreadPoolExecutor(workers) as ex:
-        res = list(ex.map(one, heads))
-    for h, xs in zip(heads, res):
-        _say(f"  head {h}: dq {xs[0]:.3f}, dk {xs[1]:.3f}, dv {xs[2]:.3f} of bound")
+        res = list(ex.map(one, pairs))
+    for bh, xs in zip(pairs, res):
+        _say(f"  {bh}: dq {xs[0]:.3f}, dk {xs[1]:.3f}, dv {xs[2]:.3f} of bound")
         for name_, x in zip(("dq", "dk", "dv"), xs):
-            assert x <= 1.0, f"head {h}: {name_} error reaches {x:.3f} of its bound"
+            assert x <= 1.0, f"{bh}: {name_} error reaches {x:.3f} of its bound"
+
+
+def test_backward_full_size_identity(full_size_backward):
+    _identity(full_size_backward)
+
+
+@pytest.mark.parametrize("first", [0, 8, 16, 24])
+def test_backward_full_size_every_element(full_size_backward, first):
+    """Heads first .. first+7 of the headline shape (B = 1, 32 heads)."""
+    w = full_size_backward[0]
+    _every_element(full_size_backward, [(0, h) for h in range(first, min(first + 8, w.H))])
+
+
+def test_backward_d256_full_size_identity(full_size_backward_d256):
+    _identity(full_size_backward_d256)
+
+
+@pytest.mark.parametrize("first", [0, 16, 32, 48])
+def test_backward_d256_full_size_every_element(full_size_backward_d256, first):
+    """(batch, head) slices first .. first+15 of the 64 of the d = 256
+    workload (B = 4, H = 16)."""
+    w = full_size_backward_d256[0]
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)][first:first + 16]
+    _every_element(full_size_backward_d256, pairs)
