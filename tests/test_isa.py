@@ -10,6 +10,10 @@ device assembly with the library's own flags; nothing runs on a GPU).
   anywhere: every source is built with that target feature switched off.
 * The forward, backward and decode kernels keep everything in registers and
   LDS (no scratch spills).
+* In the backward's wave-pair dK/dV kernel every LDS write (the fp32 tiles
+  the two waves of a pair exchange) is complete before the next barrier: on
+  this part the compiler puts no wait in front of s_barrier, so the kernel
+  waits by hand, and the partner's read after the barrier relies on it.
 """
 import os
 import re
@@ -64,3 +68,38 @@ def test_no_scratch_spills(asm, src):
     sizes = [int(m.group(1)) for m in
              (re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", ln) for ln in asm[src]) if m]
     assert sizes and max(sizes) == 0, f"{src}: private segment sizes {sorted(set(sizes))}"
+
+
+def _kernel_bodies(lines, name):
+    """Code lines of each kernel whose symbol contains name."""
+    bodies, cur = [], None
+    for ln in lines:
+        if re.match(r"^_Z\S*:", ln):
+            cur = [] if name in ln else None
+            if cur is not None:
+                bodies.append(cur)
+        elif cur is not None:
+            if ln.strip().startswith(".end_amdhsa_kernel") or "s_endpgm" in ln:
+                cur.append(ln)
+                cur = None
+            else:
+                cur.append(ln)
+    return bodies
+
+
+def test_pair_kernel_lds_writes_complete_before_each_barrier(asm):
+    bodies = _kernel_bodies(asm["fa_bwd_mfma.hip"], "fa_bwd_dkdv_pair_kernel")
+    assert bodies, "no wave-pair dK/dV kernel in the backward's code"
+    writes = 0
+    for body in bodies:
+        code = list(_code(body))
+        for k, (i, t) in enumerate(code):
+            if not t.startswith("ds_write"):
+                continue
+            writes += 1
+            for _, u in code[k + 1:]:
+                if u.startswith("s_waitcnt") and "lgkmcnt(0)" in u:
+                    break
+                assert not u.startswith("s_barrier"), \
+                    f"LDS write at line {i + 1} ({t}) not awaited before a barrier"
+    assert writes > 0
