@@ -107,12 +107,21 @@ def test_backward_full(dtype, d, mask, H, Hkv, S, window):
 
 @pytest.mark.parametrize("S", [1, 2, 31, 32, 33, 127, 128, 129])
 @pytest.mark.parametrize("mask", ["none", "causal"])
-def test_backward_short_sequences(S, mask):
-    _check(1, 2, 2, S, 128, "bf16", mask)
+@pytest.mark.parametrize("d", [128, 256])
+def test_backward_short_sequences(S, mask, d):
+    # at d = 256: one or two 64-key work-groups, keys and rows past S zero-filled
+    _check(1, 2, 2, S, d, "bf16", mask)
 
 
-def test_backward_batch():
-    _check(3, 2, 1, 190, 64, "bf16", "causal")
+@pytest.mark.parametrize("d", [64, 256])
+def test_backward_batch(d):
+    _check(3, 2, 1, 190, d, "bf16", "causal")
+
+
+@pytest.mark.parametrize("window", [1, 63, 64, 65])
+def test_backward_d256_window_edges(window):
+    """Windows around the 64-key work-group and 32-key wave-pair widths."""
+    _check(1, 2, 1, 250, 256, "f16", "window", window)
 
 
 @pytest.mark.parametrize("scale", [0.02, 1.0, -0.1])
