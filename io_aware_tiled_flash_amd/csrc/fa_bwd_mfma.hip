@@ -18,7 +18,11 @@
 //   * dK/dV: one work-group per 128 keys of one key/value head; each wave
 //     owns 32 keys, keeps their K and V rows in registers as MFMA operands
 //     and streams the query tiles (Q, dO, LSE, D through LDS) of every query
-//     head that reads this key/value head;
+//     head that reads this key/value head.  At d = 256 (where K, V and
+//     whole-d accumulators exceed a wave's registers) one work-group per 64
+//     keys, whose waves work in pairs: one computes S, the other dP, they
+//     exchange the fp32 tiles through LDS and each accumulates dK and dV for
+//     half of the columns;
 //   * dQ: one work-group per 128 query rows; each wave owns 32 rows, keeps
 //     their Q and dO rows in registers and streams K/V tiles through LDS, as
 //     the forward kernel does.
