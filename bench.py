@@ -61,6 +61,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # summary is only used while these are unchanged.
 FWD_SOURCES = ("fa_fwd_mfma.hip", "fa_gfx950.h", "fa_internal.h")
 DECODE_SOURCES = ("fa_decode.hip", "fa_tile_ops.h", "fa_gfx950.h", "fa_internal.h")
+BWD_SOURCES = ("fa_bwd_mfma.hip", "fa_tile_ops.h", "fa_gfx950.h", "fa_internal.h")
 
 
 def kernel_source_digest(sources=FWD_SOURCES) -> str:
@@ -597,7 +598,9 @@ def main(argv=None) -> int:
     flops = w.flops() * (BWD_FLOP_RATIO if bwd else 1.0)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = None if bwd else measured_traffic(w.name)
+    # the backward's traffic is that of its dominant launch, the dK/dV kernel
+    traffic = (measured_traffic(f"{w.name}_bwd_dkdv", BWD_SOURCES) if bwd
+               else measured_traffic(w.name))
     if bwd:
         metric = (f"attention bwd TFLOP/s on {w.name} (10*d FLOPs per visible pair); "
                   f"% of MFMA {w.dtype} peak")
@@ -651,7 +654,8 @@ def main(argv=None) -> int:
     issued_ratio = 1.0
     if bwd:
         issued_ratio = BWD_ISSUED_RATIO
-        result["roofline"]["scope"] = "whole pass (three launches)"
+        result["roofline"]["scope"] = ("whole pass (three launches); traffic: HBM bytes of "
+                                       "one dK/dV launch")
         result["roofline"]["mfma_flop_issued_per_credited"] = issued_ratio
     if args.ceiling and w.dtype in ("bf16", "f16"):
         ceil = mfma_ceiling(dev, stream, w.dtype, clock)

@@ -143,8 +143,16 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int lq = lane & 31, lg = lane >> 5;
   const int S = a.S, H = a.H, Hkv = a.Hkv, group = H / Hkv;
   const int n_kv = a.B * Hkv;
-  const int kvi = blockIdx.x % n_kv;  // key/value head (b * Hkv + hk)
-  const int kt = blockIdx.x / n_kv;   // key tile; the first ones see the most rows
+  int kvi = blockIdx.x % n_kv;  // key/value head (b * Hkv + hk)
+  int kt = blockIdx.x / n_kv;   // key tile; the first ones see the most rows
+  if (MASK == kMaskNone && n_kv % 8 == 0) {
+    // no imbalance to order by: each XCD (work-group b goes to XCD b % 8)
+    // runs a head's key tiles in a row, so they share its query stream in
+    // that XCD's L2
+    const int nkt = gridDim.x / n_kv, xcd = blockIdx.x % 8, l = blockIdx.x / 8;
+    kvi = (l / nkt) * 8 + xcd;
+    kt = l % nkt;
+  }
   const int b = kvi / Hkv, hk = kvi - b * Hkv;
   const int k0 = kt * BKV, kw0 = k0 + 32 * wave;
   const float c = a.scale_log2;
@@ -474,8 +482,16 @@ __global__ __launch_bounds__(NP * 128, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a
   const int lq = lane & 31, lg = lane >> 5;
   const int S = a.S, H = a.H, Hkv = a.Hkv, group = H / Hkv;
   const int n_kv = a.B * Hkv;
-  const int kvi = blockIdx.x % n_kv;  // key/value head (b * Hkv + hk)
-  const int kt = blockIdx.x / n_kv;   // key tile; the first ones see the most rows
+  int kvi = blockIdx.x % n_kv;  // key/value head (b * Hkv + hk)
+  int kt = blockIdx.x / n_kv;   // key tile; the first ones see the most rows
+  if (MASK == kMaskNone && n_kv % 8 == 0) {
+    // no imbalance to order by: each XCD (work-group b goes to XCD b % 8)
+    // runs a head's key tiles in a row, so they share its query stream in
+    // that XCD's L2
+    const int nkt = gridDim.x / n_kv, xcd = blockIdx.x % 8, l = blockIdx.x / 8;
+    kvi = (l / nkt) * 8 + xcd;
+    kt = l % nkt;
+  }
   const int b = kvi / Hkv, hk = kvi - b * Hkv;
   const int k0 = kt * BKV, kw0 = k0 + 32 * pair;
   const float c = a.scale_log2;
@@ -830,8 +846,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_bwd_dq_kernel(BwdArgs a) {
   const int S = a.S;
   const int BH = a.B * a.H;
   const int nqt = (S + BR - 1) / BR;
-  const HeadPair hp = head_of_slot(blockIdx.x % BH, a.B, a.H, a.Hkv);
-  int qt = blockIdx.x / BH;
+  int slot = blockIdx.x % BH, qt = blockIdx.x / BH;
+  if (MASK == kMaskNone && BH % 8 == 0) {
+    // each XCD runs a head's query tiles in a row (shared K/V in its L2)
+    const int xcd = blockIdx.x % 8, l = blockIdx.x / 8;
+    slot = (l / nqt) * 8 + xcd;
+    qt = l % nqt;
+  }
+  const HeadPair hp = head_of_slot(slot, a.B, a.H, a.Hkv);
   if (MASK != kMaskNone) qt = nqt - 1 - qt;  // heaviest query tiles first
   const int q0 = qt * BR, wr0 = q0 + 32 * wave, wr1 = wr0 + 31;
   const int row = wr0 + lq;  // this lane's query row
