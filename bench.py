@@ -526,7 +526,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the per-head work needs no exchange; see the sharding notes in the design "
               "document). Run with --gpus 1.", file=sys.stderr)
         return 2
