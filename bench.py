@@ -527,8 +527,9 @@ def main(argv=None) -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the per-head work needs no exchange; see the sharding notes in the design "
-              "document). Run with --gpus 1.", file=sys.stderr)
+              "(each head's work needs no exchange with another's, so a multi-GPU run "
+              "would shard by batch and heads, one share per GPU). Run with --gpus 1.",
+              file=sys.stderr)
         return 2
     if args.graph and args.pass_ != "fwd":
         print("--graph times the forward pass only", file=sys.stderr)
