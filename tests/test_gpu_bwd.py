@@ -92,7 +92,11 @@ CASES = [
     ("f16", 64, "none", 6, 3, 257, None),
     ("bf16", 128, "causal", 4, 1, 200, None),   # one shared key/value head
     ("bf16", 128, "window", 4, 2, 333, 50),
-    # d = 256: two dK/dV work-groups per key tile, each owning half of d
+    # unmasked with a multiple of 8 key/value heads: tiles of a head run in a
+    # row on one XCD (the other unmasked cases keep the plain order)
+    ("bf16", 128, "none", 8, 8, 300, None),
+    ("f16", 64, "none", 16, 8, 200, None),
+    # d = 256: wave pairs, each wave owning half of d for dK and dV
     ("bf16", 256, "causal", 2, 2, 300, None),
     ("f16", 256, "none", 1, 1, 200, None),
     ("bf16", 256, "window", 4, 2, 333, 70),
